@@ -1,0 +1,222 @@
+"""Benchmark of the OTT decode step on one MI355X.
+
+A step is the whole hot path for one batch: append one token per sequence,
+quantize any full window, decode one query per (sequence, query head).
+Default workload: Llama-2-7B-shaped layer, batch 32, 32 heads, ragged context
+3072-4096, G=128, R=32, P=32. Several identical, independent layer states are
+stepped round-robin so that consecutive steps touch different memory (the
+256 MB Infinity Cache cannot hold the working set between visits).
+
+Prints one JSON line (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "OTT decode-attention tokens/s + achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+DECODE_SOURCES = ("decode_attention_ott_amd/csrc/ott_kernels.hip",)
+
+
+def algorithmic_decode_bytes(layer) -> int:
+    """Bytes one decode must move: per (sequence, KV head) 512 per page (K min/scale),
+    68 per quantized token (32 B K codes + 32 B V codes + 4 B V min/scale), 512 per
+    fp16 pool or window token (K and V); plus 512 per query head (q in, out)."""
+    total = 0
+    for b in range(layer.B):
+        L, r_cnt, _, nb = layer.seq_state(b)
+        pc = min(layer.P, layer.G * nb)
+        nq = L - pc - r_cnt
+        total += layer.Hkv * (512 * nb + 68 * nq + 512 * (pc + r_cnt))
+    return total + 512 * layer.B * layer.Hq
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, lengths, budget_s: float = 12.0):
+    """The oracle, single-threaded, on a bounded sample: whole (sequence, KV head)
+    units taken in order until the time budget is spent; each runs prefill
+    (untimed) then decode steps (append + quantize + decode of every query head
+    of the unit). Scaled to the full batch: tokens/s = B / (per-unit step time
+    * B * Hkv)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import synth
+    from oracle import ott_oracle as O
+    nq = w.num_q_heads // w.num_kv_heads
+    steps = 8
+    t_step, n_unit = 0.0, 0
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t_all = time.perf_counter()
+    try:
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                K, V = synth.kv_stream(w, b, h, int(lengths[b]) + steps)
+                st = O.HeadOracle(w.head_dim, w.group_size, w.residual, w.pool_size)
+                O.run_prefill(st, K[:lengths[b]], V[:lengths[b]])
+                qs = [synth.query(w, t, b)[h * nq:(h + 1) * nq] for t in range(steps)]
+                sm = 1.0 / np.sqrt(w.head_dim)
+                t0 = time.perf_counter()
+                for t in range(steps):
+                    O.step(st, K[lengths[b] + t], V[lengths[b] + t])
+                    for i in range(nq):
+                        st.decode(qs[t][i], sm)
+                t_step += (time.perf_counter() - t0) / steps
+                n_unit += 1
+                if time.perf_counter() - t_all > budget_s:
+                    break
+            if time.perf_counter() - t_all > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    per_unit = t_step / n_unit
+    full_step = per_unit * w.batch * w.num_kv_heads
+    return {"value": w.batch / full_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_unit} (sequence, KV head) units of {w.name} x {steps} decode steps "
+                      f"(append+quantize+decode of {nq} query head(s)), fp64 numpy, 1 thread; "
+                      f"scaled to {w.batch}x{w.num_kv_heads} units",
+            "s_per_step": full_step}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="llama2-7b-b32")
+    ap.add_argument("--states", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this OTT build has no multi-GPU path "
+              "(each (sequence, KV head) is independent; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from decode_attention_ott_amd import OTTLayer, _lib as L
+
+    w = synth.WORKLOADS[args.workload]
+    lengths = synth.prefill_lengths(w)
+    n_steps_state = (args.warmup + args.steps + args.states - 1) // args.states + 1
+    n_pos = int(lengths.max()) + n_steps_state
+    print(f"[bench] generating {w.name} inputs ({n_pos} positions)", file=sys.stderr, flush=True)
+    K, V = synth.kv_all(w, n_pos)
+    dev = torch.device("cuda:0")
+    Kd = torch.from_numpy(K).to(dev)
+    Vd = torch.from_numpy(V).to(dev)
+    layers = []
+    for i in range(args.states):
+        lay = OTTLayer.for_workload(w, max_seq_len=n_pos)
+        lay.prefill(Kd, Vd, lengths)
+        layers.append(lay)
+        print(f"[bench] state {i} prefilled", file=sys.stderr, flush=True)
+    # per-state new tokens and queries, resident on the device
+    bidx = np.arange(w.batch)
+    kt = np.stack([K[bidx, :, lengths + t][:, :, None, :] for t in range(n_steps_state)])
+    vt = np.stack([V[bidx, :, lengths + t][:, :, None, :] for t in range(n_steps_state)])
+    ktd = torch.from_numpy(np.ascontiguousarray(kt)).to(dev)
+    vtd = torch.from_numpy(np.ascontiguousarray(vt)).to(dev)
+    qd = torch.from_numpy(np.stack([synth.queries(w, t) for t in range(args.warmup + args.steps)])).to(dev)
+    outd = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float16, device=dev)
+    del Kd, Vd
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    ones = [1] * w.batch
+
+    def step(i):
+        lay = layers[i % args.states]
+        t = i // args.states
+        L.ott_append(lay.handle, ktd[t].data_ptr(), vtd[t].data_ptr(), ones, 1, sp)
+        L.ott_quantize_group(lay.handle, sp)
+        return lay
+
+    for i in range(args.warmup):
+        lay = step(i)
+        L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    alg_bytes = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for j in range(args.steps):
+        i = args.warmup + j
+        lay = step(i)
+        ev[j][0].record(stream)
+        L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
+        ev[j][1].record(stream)
+        alg_bytes.append(algorithmic_decode_bytes(lay))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = w.batch * args.steps / (total_ms / 1e3)
+    achieved = sum(alg_bytes) / (sum(dec_ms) / 1e3) / 1e9
+    traffic = load_traffic(w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "decode_kernel<128>" + (" + combine_kernel" if False else ""),
+                "decode_us_mean": round(1e3 * sum(dec_ms) / len(dec_ms), 2),
+                "decode_us_median": round(1e3 * float(np.median(dec_ms)), 2),
+                "alg_bytes_per_launch": int(np.mean(alg_bytes))}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, lengths)
+    res = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+           "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                      "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                      "context": f"{w.prefill[0]}-{w.prefill[1]}", "G": w.group_size,
+                      "R": w.residual, "P": w.pool_size, "states": args.states,
+                      "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window"},
+           "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

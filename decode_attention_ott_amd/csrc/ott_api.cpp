@@ -1,0 +1,274 @@
+// Host side of the OTT C ABI: validation, arena map, host copies of the
+// per-sequence counters, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <vector>
+
+#include "../../include/ott.h"
+#include "ott_kernels.h"
+
+struct ott_ctx {
+  ott_config_t cfg;
+  ott_layout_t lay;
+  ott::Arena dev;
+  std::vector<int32_t> L, rcnt, head, nb;  // identical for every KV head of a sequence
+  int32_t forced_splits = 0;
+  bool poisoned = false;
+};
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+ott_status_t validate_config(const ott_config_t* c) {
+  if (!c) return OTT_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1 || c->max_seq_len < 1 ||
+      c->residual < 0 || c->pool_size < 0 || c->group_size < 1 || c->head_dim < 1)
+    return OTT_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return OTT_ERR_INVALID_ARG;
+  if (!(c->sm_scale == c->sm_scale)) return OTT_ERR_INVALID_ARG;  // NaN
+  if (c->batch > ott::kMaxBatch) return OTT_ERR_UNSUPPORTED;
+  if (c->head_dim != ott::kHeadDim) return OTT_ERR_UNSUPPORTED;
+  if (c->group_size != 64 && c->group_size != 128 && c->group_size != 256)
+    return OTT_ERR_UNSUPPORTED;
+  if (c->pool_size > 512 || c->residual > 4096) return OTT_ERR_UNSUPPORTED;
+  const int nq = c->num_q_heads / c->num_kv_heads;
+  if (!(nq == 1 || nq == 2 || nq % 4 == 0) || nq > 64) return OTT_ERR_UNSUPPORTED;
+  const int64_t heads = int64_t(c->batch) * c->num_kv_heads;
+  if (heads > (1 << 20)) return OTT_ERR_UNSUPPORTED;
+  return OTT_OK;
+}
+
+int max_splits_for(const ott_config_t* c) {
+  const int64_t heads = int64_t(c->batch) * c->num_kv_heads;
+  int64_t s = (1024 + heads - 1) / heads;
+  return int(std::max<int64_t>(1, std::min<int64_t>(64, s)));
+}
+
+void fill_layout(const ott_config_t* c, ott_layout_t* L) {
+  const uint64_t B = c->batch, Hkv = c->num_kv_heads, Hq = c->num_q_heads, d = c->head_dim;
+  const uint64_t G = c->group_size, P = c->pool_size, C = c->residual + c->group_size;
+  const uint64_t BH = B * Hkv;
+  const uint64_t NB = (uint64_t(c->max_seq_len) + G - 1) / G;
+  *L = ott_layout_t{};
+  L->page_bytes = G * d / 4 + d * G / 4 + 4 * d + 4 * G;
+  L->pages_per_head = int32_t(NB);
+  L->ring_capacity = int32_t(C);
+  L->max_splits = max_splits_for(c);
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L->off_counters = take(BH * 4 * sizeof(int32_t));
+  L->off_pages = take(BH * NB * L->page_bytes);
+  L->off_page_pos = take(BH * NB * G * sizeof(int32_t));
+  L->off_page_nvalid = take(BH * NB * sizeof(int32_t));
+  L->off_pool_k = take(2 * BH * P * d * 2);
+  L->off_pool_v = take(2 * BH * P * d * 2);
+  L->off_pool_pos = take(2 * BH * P * sizeof(int32_t));
+  L->off_pool_n2 = take(2 * BH * P * sizeof(double));
+  L->off_ring_k = take(BH * C * d * 2);
+  L->off_ring_v = take(BH * C * d * 2);
+  L->off_partials = take(B * Hq * uint64_t(L->max_splits) * (2 + d) * sizeof(float));
+  L->arena_bytes = off;
+}
+
+ott_status_t check_handle(ott_handle_t h) {
+  if (!h) return OTT_ERR_INVALID_ARG;
+  if (h->poisoned) return OTT_ERR_HIP;
+  return OTT_OK;
+}
+
+ott_status_t after_launch(ott_handle_t h, hipError_t e) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    h->poisoned = true;
+    return OTT_ERR_HIP;
+  }
+  return OTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes,
+                      size_t* required_bytes, ott_handle_t* out) {
+  ott_status_t st = validate_config(cfg);
+  if (st != OTT_OK) return st;
+  ott_layout_t lay;
+  fill_layout(cfg, &lay);
+  if (required_bytes) *required_bytes = size_t(lay.arena_bytes);
+  if (!d_arena) {
+    if (out) return OTT_ERR_INVALID_ARG;  // creating a handle needs an arena
+    if (!required_bytes) return OTT_ERR_INVALID_ARG;
+    return OTT_OK;
+  }
+  if (!out) return OTT_ERR_INVALID_ARG;
+  if (arena_bytes < lay.arena_bytes || (reinterpret_cast<uintptr_t>(d_arena) % kAlign) != 0)
+    return OTT_ERR_ARENA_TOO_SMALL;
+
+  ott_ctx* h = new (std::nothrow) ott_ctx();
+  if (!h) return OTT_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  if (h->cfg.sm_scale <= 0.f) h->cfg.sm_scale = 1.0f / std::sqrt(float(cfg->head_dim));
+  h->lay = lay;
+  ott::Arena& a = h->dev;
+  a.base = static_cast<uint8_t*>(d_arena);
+  a.B = cfg->batch;
+  a.Hq = cfg->num_q_heads;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = cfg->group_size;
+  a.R = cfg->residual;
+  a.P = cfg->pool_size;
+  a.C = cfg->residual + cfg->group_size;
+  a.nb_max = lay.pages_per_head;
+  a.max_splits = lay.max_splits;
+  a.page_bytes = uint32_t(lay.page_bytes);
+  a.off_counters = lay.off_counters;
+  a.off_pages = lay.off_pages;
+  a.off_page_pos = lay.off_page_pos;
+  a.off_page_nvalid = lay.off_page_nvalid;
+  a.off_pool_k = lay.off_pool_k;
+  a.off_pool_v = lay.off_pool_v;
+  a.off_pool_pos = lay.off_pool_pos;
+  a.off_pool_n2 = lay.off_pool_n2;
+  a.off_ring_k = lay.off_ring_k;
+  a.off_ring_v = lay.off_ring_v;
+  a.off_partials = lay.off_partials;
+  a.sm_scale = h->cfg.sm_scale;
+  const size_t nb = size_t(cfg->batch);
+  h->L.assign(nb, 0);
+  h->rcnt.assign(nb, 0);
+  h->head.assign(nb, 0);
+  h->nb.assign(nb, 0);
+  const size_t ctr_bytes = size_t(cfg->batch) * cfg->num_kv_heads * 4 * sizeof(int32_t);
+  if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess) {
+    delete h;
+    return OTT_ERR_HIP;
+  }
+  *out = h;
+  return OTT_OK;
+}
+
+ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const int32_t* h_n_new,
+                        int32_t max_new, void* stream) {
+  ott_status_t st = check_handle(h);
+  if (st != OTT_OK) return st;
+  if (!h_n_new || max_new < 0) return OTT_ERR_INVALID_ARG;
+  const int B = h->cfg.batch;
+  const int C = h->dev.C;
+  bool any = false, uniform = true;
+  for (int b = 0; b < B; ++b) {
+    const int n = h_n_new[b];
+    if (n < 0 || n > max_new) return OTT_ERR_INVALID_ARG;
+    if (n != h_n_new[0]) uniform = false;
+    if (n > 0) any = true;
+  }
+  if (!any) return OTT_OK;
+  if (!d_k || !d_v) return OTT_ERR_INVALID_ARG;
+  for (int b = 0; b < B; ++b) {
+    const int n = h_n_new[b];
+    if (h->rcnt[b] + n > C) return OTT_ERR_CAPACITY;
+    if (int64_t(h->L[b]) + n > h->cfg.max_seq_len) return OTT_ERR_CAPACITY;
+  }
+  ott::AppendCounts cnt{};
+  cnt.max_new = max_new;
+  cnt.uniform = uniform ? h_n_new[0] : -1;
+  for (int b = 0; b < B; ++b) cnt.n[b] = uint16_t(h_n_new[b]);
+  st = after_launch(h, ott::launch_append(h->dev, d_k, d_v, cnt, static_cast<hipStream_t>(stream)));
+  if (st != OTT_OK) return st;
+  for (int b = 0; b < B; ++b) {
+    h->L[b] += h_n_new[b];
+    h->rcnt[b] += h_n_new[b];
+  }
+  return OTT_OK;
+}
+
+ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_quantized) {
+  ott_status_t st = check_handle(h);
+  if (st != OTT_OK) return st;
+  const int B = h->cfg.batch, C = h->dev.C, G = h->dev.G;
+  int ready = 0;
+  for (int b = 0; b < B; ++b) ready += (h->rcnt[b] >= C);
+  if (n_seq_quantized) *n_seq_quantized = 0;
+  if (ready == 0) return OTT_OK;
+  st = after_launch(h, ott::launch_quantize(h->dev, static_cast<hipStream_t>(stream)));
+  if (st != OTT_OK) return st;
+  for (int b = 0; b < B; ++b) {
+    if (h->rcnt[b] >= C) {
+      h->head[b] = (h->head[b] + G) % C;
+      h->rcnt[b] -= G;
+      h->nb[b] += 1;
+    }
+  }
+  if (n_seq_quantized) *n_seq_quantized = ready;
+  return OTT_OK;
+}
+
+ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream) {
+  ott_status_t st = check_handle(h);
+  if (st != OTT_OK) return st;
+  if (!d_q || !d_out) return OTT_ERR_INVALID_ARG;
+  const int B = h->cfg.batch;
+  int units_max = 0;
+  for (int b = 0; b < B; ++b) {
+    if (h->L[b] == 0) return OTT_ERR_STATE;
+    const int pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
+    const int units = h->nb[b] + (pc + h->rcnt[b] + ott::kFp16Chunk - 1) / ott::kFp16Chunk;
+    units_max = std::max(units_max, units);
+  }
+  int S = h->forced_splits;
+  if (S <= 0) {
+    const int heads = B * h->cfg.num_kv_heads;
+    S = (heads >= 512) ? 1 : (1024 + heads - 1) / heads;
+    S = std::min(S, std::max(1, units_max / 4));
+  }
+  S = std::max(1, std::min(S, h->dev.max_splits));
+  return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, static_cast<hipStream_t>(stream)));
+}
+
+void ott_destroy(ott_handle_t h) { delete h; }
+
+ott_status_t ott_get_layout(ott_handle_t h, ott_layout_t* out) {
+  if (!h || !out) return OTT_ERR_INVALID_ARG;
+  *out = h->lay;
+  return OTT_OK;
+}
+
+ott_status_t ott_get_seq_state(ott_handle_t h, int32_t b, int32_t out[4]) {
+  if (!h || !out || b < 0 || b >= h->cfg.batch) return OTT_ERR_INVALID_ARG;
+  out[0] = h->L[b];
+  out[1] = h->rcnt[b];
+  out[2] = h->head[b];
+  out[3] = h->nb[b];
+  return OTT_OK;
+}
+
+ott_status_t ott_set_num_splits(ott_handle_t h, int32_t num_splits) {
+  if (!h || num_splits < 0 || num_splits > h->lay.max_splits) return OTT_ERR_INVALID_ARG;
+  h->forced_splits = num_splits;
+  return OTT_OK;
+}
+
+const char* ott_status_string(ott_status_t s) {
+  switch (s) {
+    case OTT_OK: return "ok";
+    case OTT_ERR_INVALID_ARG: return "invalid argument";
+    case OTT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case OTT_ERR_ARENA_TOO_SMALL: return "arena too small or misaligned";
+    case OTT_ERR_CAPACITY: return "window or sequence capacity exceeded";
+    case OTT_ERR_STATE: return "invalid state for this call";
+    case OTT_ERR_HIP: return "HIP error (handle poisoned)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

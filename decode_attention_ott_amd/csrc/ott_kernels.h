@@ -1,0 +1,41 @@
+// Internal interface between the host library (ott_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ott {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxBatch = 512;
+constexpr int kFp16Chunk = 64;  // window/pool tokens handled per decode work unit
+
+// Device view of one handle's arena. Passed by value to every kernel.
+struct Arena {
+  uint8_t* base;
+  int32_t B, Hq, Hkv, G, R, P, C;  // C = R + G (window ring capacity)
+  int32_t nb_max;                  // pages per (sequence, KV head)
+  int32_t max_splits;
+  uint32_t page_bytes;
+  uint64_t off_counters, off_pages, off_page_pos, off_page_nvalid;
+  uint64_t off_pool_k, off_pool_v, off_pool_pos, off_pool_n2;
+  uint64_t off_ring_k, off_ring_v, off_partials;
+  float sm_scale;
+};
+
+// New-token counts of one ott_append call (uint16 keeps the kernel argument at 1 KiB).
+struct AppendCounts {
+  int32_t max_new;
+  int32_t uniform;  // >= 0: every sequence appends this many; < 0: use n[]
+  uint16_t n[kMaxBatch];
+};
+
+hipError_t launch_append(const Arena& a, const void* k, const void* v, const AppendCounts& n,
+                         hipStream_t s);
+hipError_t launch_quantize(const Arena& a, hipStream_t s);
+hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits, hipStream_t s);
+
+// Dynamic LDS bytes the quantize kernel needs for (G, P).
+size_t quantize_lds_bytes(int G, int P);
+
+}  // namespace ott

@@ -1,0 +1,188 @@
+/*
+ * ott.h - C ABI of the MI355X (gfx950) Outlier Tokens Tracing decode-attention library.
+ *
+ * The method: "Accurate KV Cache Quantization with Outlier Tokens Tracing"
+ * (arXiv 2505.10938). Passages are cited by page and section:
+ *   [Blog] zijie-tian.site summary page: section 3.1 (group quantization every G
+ *          tokens, Key-norm outlier rule), 3.2 (Outlier Pool), 3.3 (three caches,
+ *          one fused decode) and its flowchart; section 4 (defaults G=128, R=32).
+ *   [Abs]  sciencestack.ai page: TL;DR; Abstract (Keys per channel, Values per
+ *          token); Figure 1(c) (smallest Key magnitude is the retention rule);
+ *          Figure 2 (decoding stage on top, quantization stage below).
+ *
+ * One handle serves one attention layer: B sequences, Hkv KV heads, Hq query
+ * heads (Hq a multiple of Hkv), head_dim 128. Each (sequence, KV head) owns
+ *   - a 2-bit quantized cache of pages, one page per quantized group,
+ *   - an outlier pool of up to P fp16 tokens (smallest squared Key L2 norm),
+ *   - an fp16 residual window (a ring of R+G slots) of unquantized tokens.
+ * A decode step is: ott_append (one token per sequence), ott_quantize_group
+ * (a no-op unless some window is full), ott_decode.
+ *
+ * Ownership: the caller owns all device memory - the arena and every input and
+ * output buffer. The library allocates no device memory and never synchronizes
+ * a stream; it only enqueues kernels on the stream it is given. The host
+ * handle is the library's; ott_destroy frees it.
+ * Errors: every call returns a status and validates its arguments before it
+ * enqueues anything, so a rejected call leaves the state unchanged. A failed
+ * kernel launch poisons the handle: later calls return OTT_ERR_HIP.
+ * Threading: a handle is not thread-safe; calls on one handle must be issued
+ * in order, on one stream or with the caller ordering the streams.
+ * Streams are passed as `void*` holding a hipStream_t (NULL = default stream).
+ */
+#ifndef OTT_H_
+#define OTT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ott_ctx* ott_handle_t;
+
+typedef enum {
+  OTT_OK = 0,
+  OTT_ERR_INVALID_ARG = 1,     /* NULL pointer, out-of-range value */
+  OTT_ERR_UNSUPPORTED = 2,     /* valid but not built: head_dim != 128, G not 64/128/256, ... */
+  OTT_ERR_ARENA_TOO_SMALL = 3, /* arena_bytes below the required size, or misaligned arena */
+  OTT_ERR_CAPACITY = 4,        /* append would overflow the window or max_seq_len */
+  OTT_ERR_STATE = 5,           /* decode of a sequence that holds no token */
+  OTT_ERR_HIP = 6              /* a HIP launch failed; the handle is poisoned */
+} ott_status_t;
+
+/* Layer shape and OTT hyper-parameters ([Blog] 3.1-3.3, section 4 and 6). */
+typedef struct {
+  int32_t batch;        /* B, 1..512 */
+  int32_t num_q_heads;  /* Hq, a multiple of Hkv; Hq/Hkv must be 1, 2 or a multiple of 4 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* d, must be 128 */
+  int32_t group_size;   /* G: tokens per quantized group, 64, 128 or 256 */
+  int32_t residual;     /* R >= 0: tokens always kept in the fp16 window */
+  int32_t pool_size;    /* P, 0..512: outlier-pool capacity (0 = plain 2-bit cache) */
+  int32_t max_seq_len;  /* tokens a sequence may reach, >= 1 */
+  float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+} ott_config_t;
+
+/*
+ * Arena map (byte offsets from the arena base; every region is 256-byte aligned).
+ * "bh" is b*Hkv + kvh. "NB" is pages_per_head = ceil(max_seq_len / G).
+ *   counters   int32 [B*Hkv][4]: {L, r_cnt, ring_head, nb} of each (sequence, KV head)
+ *   pages      [B*Hkv][NB][page_bytes], page n = the n-th quantized group, laid out as
+ *                K codes  [G tokens][d/4 bytes], token-major: byte j of token t holds
+ *                         channels 4j..4j+3, channel 4j+i in bits 2i..2i+1;
+ *                V codes  [d channels][G/4 bytes], channel-major: byte j of channel c
+ *                         holds slots 4j..4j+3, slot 4j+i in bits 2i..2i+1;
+ *                K meta   [d] x {fp16 min, fp16 scale}   (per channel, [Abs] Abstract);
+ *                V meta   [G] x {fp16 min, fp16 scale}   (per token,  [Abs] Abstract);
+ *              members are in position order, slots >= n_valid are all-zero bytes.
+ *              page_bytes = G*d/4 + d*G/4 + 4*d + 4*G (9216 at G=128, d=128).
+ *   page_pos   int32 [B*Hkv][NB][G]: member positions (-1 past n_valid); tests only
+ *   page_nvalid int32 [B*Hkv][NB]: members per page; tests only
+ *   pool_k, pool_v   fp16  [2][B*Hkv][P][d]
+ *   pool_pos         int32 [2][B*Hkv][P]
+ *   pool_n2          fp64  [2][B*Hkv][P]   squared Key norm of each pool token
+ *              two buffers: after nb quantize steps the live pool is buffer (nb & 1);
+ *              its first min(P, G*nb) slots are used, ascending (norm, position).
+ *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
+ *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
+ *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states.
+ */
+typedef struct {
+  uint64_t arena_bytes;
+  uint64_t page_bytes;
+  int32_t pages_per_head;
+  int32_t ring_capacity;
+  int32_t max_splits;
+  int32_t reserved0;
+  uint64_t off_counters;
+  uint64_t off_pages;
+  uint64_t off_page_pos;
+  uint64_t off_page_nvalid;
+  uint64_t off_pool_k;
+  uint64_t off_pool_v;
+  uint64_t off_pool_pos;
+  uint64_t off_pool_n2;
+  uint64_t off_ring_k;
+  uint64_t off_ring_v;
+  uint64_t off_partials;
+} ott_layout_t;
+
+/*
+ * ott_init - validate a config, size the arena, and create a handle.
+ *   Sizing: pass d_arena = NULL and out = NULL; *required_bytes receives the size.
+ *   Create: pass a device arena of >= required bytes (256-byte aligned); *out
+ *   receives the handle. The per-(sequence, head) counters are zeroed with a
+ *   blocking hipMemset on the default stream; nothing else is touched.
+ *   required_bytes may be NULL when creating.
+ */
+ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes,
+                      size_t* required_bytes, ott_handle_t* out);
+
+/*
+ * ott_append - add new tokens to each sequence's fp16 window ([Blog] 3.3: the
+ * residual window keeps recent tokens in FP16).
+ *   d_k, d_v : device fp16 [B][Hkv][max_new][d]; token i of sequence b is row i
+ *              and takes position L_b + i. Copied; reusable once the stream has run.
+ *   h_n_new  : host int32 [B], 0 <= n_new[b] <= max_new.
+ *   Fails with OTT_ERR_CAPACITY (nothing enqueued) when some r_cnt_b + n_new[b]
+ *   exceeds R+G (call ott_quantize_group first) or L_b + n_new[b] > max_seq_len.
+ */
+ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const int32_t* h_n_new,
+                        int32_t max_new, void* stream);
+
+/*
+ * ott_quantize_group - the quantization stage ([Blog] 3.1-3.2 and flowchart;
+ * [Abs] Figure 2 bottom). For every sequence whose window holds R+G tokens, and
+ * for each of its KV heads, one group is processed:
+ *   the G oldest window tokens and the pool compete; the P with the smallest
+ *   squared Key norm (fp64, summed over channels 0..d-1; ties to the lower
+ *   position) form the new pool; every other candidate, evicted pool tokens
+ *   included, is quantized to 2 bits as one new page:
+ *     scale = fp16_rne(fp32(max - min) / 3), min stored as fp16,
+ *     code  = clamp(rint_half_even(fp32(x - min) / scale), 0, 3) (0 when scale is 0),
+ *   per channel over the members for Keys, per member over its d channels for Values.
+ *   *n_seq_quantized (may be NULL) receives the number of sequences processed.
+ *   A no-op (nothing enqueued) when no window is full.
+ */
+ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_quantized);
+
+/*
+ * ott_decode - the decoding stage ([Blog] flowchart and 3.3; [Abs] Figure 2 top).
+ * For each sequence b and query head qh (KV head qh / (Hq/Hkv)):
+ *   out = sum_i softmax_i(sm_scale * q.k_i) v_i over every cached token of b:
+ *   dequantized page tokens (k = min + scale*code), the fp16 pool and the fp16
+ *   window, with one softmax over all of them.
+ *   d_q   : device fp16 [B][Hq][d];  d_out : device fp16 [B][Hq][d].
+ *   The state is not modified; the call can be repeated.
+ *   OTT_ERR_STATE if some sequence holds no token.
+ */
+ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream);
+
+/* ott_destroy - free the host handle (the arena stays the caller's). NULL is a no-op. */
+void ott_destroy(ott_handle_t h);
+
+/* ott_get_layout - the arena map of a handle. */
+ott_status_t ott_get_layout(ott_handle_t h, ott_layout_t* out);
+
+/*
+ * ott_get_seq_state - host copy of sequence b's counters:
+ * out[0] = L (tokens), out[1] = r_cnt (window tokens), out[2] = ring_head,
+ * out[3] = nb (pages). Every KV head of a sequence holds the same values.
+ */
+ott_status_t ott_get_seq_state(ott_handle_t h, int32_t b, int32_t out[4]);
+
+/*
+ * ott_set_num_splits - split-K factor of ott_decode: 0 = automatic, otherwise
+ * 1..max_splits work-groups per (sequence, KV head). Results agree to rounding.
+ */
+ott_status_t ott_set_num_splits(ott_handle_t h, int32_t num_splits);
+
+/* ott_status_string - static text for a status code. */
+const char* ott_status_string(ott_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OTT_H_ */

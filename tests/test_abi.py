@@ -1,0 +1,89 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\**(ott_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    from decode_attention_ott_amd import _lib as L
+    declared = _declared_symbols()
+    assert {"ott_init", "ott_append", "ott_quantize_group", "ott_decode"} <= declared
+    assert declared == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(L.lib, name), name
+
+
+def _cfg(**kw):
+    from decode_attention_ott_amd import _lib as L
+    base = dict(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128, group_size=128, residual=32,
+                pool_size=32, max_seq_len=1000, sm_scale=0.0)
+    base.update(kw)
+    return L.ott_config_t(**base)
+
+
+def _sizing(cfg):
+    from decode_attention_ott_amd import _lib as L
+    req = ctypes.c_size_t(0)
+    st = L.lib.ott_init(ctypes.byref(cfg), None, 0, ctypes.byref(req), None)
+    return st, req.value
+
+
+def test_sizing_matches_layout_formula():
+    st, req = _sizing(_cfg())
+    assert st == 0
+    B, Hkv, Hq, d, G, R, P, NB = 2, 2, 4, 128, 128, 32, 32, 8   # NB = ceil(1000/128)
+    al = lambda x: (x + 255) // 256 * 256
+    page = G * d // 4 * 2 + 4 * d + 4 * G
+    assert page == 9216
+    S = min(64, (1024 + B * Hkv - 1) // (B * Hkv))
+    want = (al(B * Hkv * 16) + al(B * Hkv * NB * page) + al(B * Hkv * NB * G * 4)
+            + al(B * Hkv * NB * 4) + 2 * al(2 * B * Hkv * P * d * 2) + al(2 * B * Hkv * P * 4)
+            + al(2 * B * Hkv * P * 8) + 2 * al(B * Hkv * (R + G) * d * 2)
+            + al(B * Hq * S * (2 + d) * 4))
+    assert req == want
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=64), 2), (dict(group_size=96), 2), (dict(group_size=32), 2),
+    (dict(num_q_heads=3), 1), (dict(num_q_heads=6, num_kv_heads=2), 2),
+    (dict(batch=0), 1), (dict(batch=513), 2), (dict(pool_size=-1), 1), (dict(pool_size=600), 2),
+    (dict(residual=-1), 1), (dict(max_seq_len=0), 1), (dict(sm_scale=float("nan")), 1),
+])
+def test_bad_configs_are_rejected(bad, status):
+    st, _ = _sizing(_cfg(**bad))
+    assert st == status
+
+
+def test_calls_validate_before_any_gpu_work():
+    from decode_attention_ott_amd import _lib as L
+    lib = L.lib
+    cfg = _cfg()
+    h = ctypes.c_void_p(0)
+    # creating a handle without an arena is an argument error (no HIP call)
+    assert lib.ott_init(ctypes.byref(cfg), None, 0, None, ctypes.byref(h)) == 1
+    # an undersized or misaligned arena is rejected before any HIP call
+    assert lib.ott_init(ctypes.byref(cfg), ctypes.c_void_p(4096), 16, None, ctypes.byref(h)) == 3
+    assert lib.ott_init(ctypes.byref(cfg), ctypes.c_void_p(4096 + 8), 1 << 40, None,
+                        ctypes.byref(h)) == 3
+    n = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.ott_append(None, None, None, n, 1, None) == 1
+    assert lib.ott_quantize_group(None, None, None) == 1
+    assert lib.ott_decode(None, None, None, None) == 1
+    assert lib.ott_get_layout(None, None) == 1
+    assert lib.ott_set_num_splits(None, 1) == 1
+    lib.ott_destroy(None)
+    assert L.ott_status_string(4) == "window or sequence capacity exceeded"

@@ -1,0 +1,123 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: page bytes (codes and fp16 min/scale), member positions, pool
+membership/order/contents, window contents, counters. Within tolerance
+(max abs 2e-3, rel L2 1e-3): fp16 decode outputs.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.parity import check_state, log, run_case
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def small(name, B=2, Hq=2, Hkv=2, G=128, R=32, P=32, L=(400, 400), steps=8, seed=11, **kw):
+    return synth.Workload(name, B, Hq, Hkv, 128, G, R, P, L, steps, seed, **kw)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---- the tiny workload, state checked after every step ----------------------
+def test_tiny_every_step():
+    run_case(W["tiny"], state_every_step=True)
+
+
+# ---- parameter coverage on small shapes -------------------------------------
+@pytest.mark.parametrize("G,R,P,L,steps", [
+    (64, 16, 8, (300, 300), 70),      # G=64, crosses quantize steps during decode
+    (256, 64, 128, (700, 700), 12),   # G=256 with a large pool
+    (128, 32, 0, (500, 500), 40),     # P=0: plain 2-bit cache
+    (128, 0, 32, (400, 400), 12),     # R=0: the window empties at each quantize
+    (128, 32, 160, (600, 600), 8),    # P > G: first page empty
+    (64, 5, 3, (333, 333), 20),       # odd window and pool sizes
+])
+def test_parameters(G, R, P, L, steps):
+    run_case(small(f"g{G}r{R}p{P}", G=G, R=R, P=P, L=L, steps=steps, seed=G + R + P),
+             state_every_step=True)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2), (12, 3)])
+def test_grouped_query_heads(Hq, Hkv):
+    run_case(small(f"gqa{Hq}x{Hkv}", Hq=Hq, Hkv=Hkv, L=(520, 520), steps=6, seed=Hq))
+
+
+def test_ragged_and_short_sequences():
+    """Sequences of length 1 (window only), below R+G (no page), and longer."""
+    w = small("ragged", B=5, Hq=4, Hkv=2, L=(1, 1), steps=10)
+    run_case(w, lengths=[1, 50, 159, 200, 777], state_every_step=True)
+
+
+def test_split_counts_agree():
+    w = small("splits", B=2, Hq=2, Hkv=2, L=(2000, 2000), steps=3)
+    run_case(w, splits=[1, 2, 3, 7, 16, 0])
+
+
+def test_large_scores_are_safe():
+    """Queries scaled x16: scores in the hundreds; the online softmax must
+    rescale without overflow (softmax shift invariance)."""
+    run_case(small("bigq", L=(900, 900), steps=3), q_scale=16.0)
+
+
+def test_outlier_heavy_keys():
+    """Many tiny-norm tokens (5%) in heavy outlier channels: the pool churns."""
+    run_case(small("churn", L=(1500, 1500), steps=20, tok_prob=0.05, chan_scale=30.0),
+             state_every_step=True)
+
+
+def test_decode_is_deterministic_and_repeatable():
+    import torch
+    from decode_attention_ott_amd import OTTLayer
+    w = small("det", B=2, Hq=8, Hkv=2, L=(1200, 1200))
+    K, V = synth.kv_all(w, 1200)
+    layer = OTTLayer.for_workload(w, max_seq_len=1300)
+    layer.prefill(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), [1200, 1200])
+    q = torch.from_numpy(synth.queries(w, 0)).cuda()
+    outs = []
+    for s in (0, 0, 5, 5):
+        layer.set_num_splits(s)
+        outs.append(layer.decode(q).cpu().numpy().view(np.uint16))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[2], outs[3])
+
+
+def test_capacity_error_leaves_state_unchanged():
+    import torch
+    from decode_attention_ott_amd import OTTLayer, OttError
+    layer = OTTLayer(1, 1, 1, 128, 128, 32, 32, max_seq_len=400)
+    k = torch.zeros(1, 1, 160, 128, dtype=torch.float16, device="cuda")
+    layer.append(k, k)
+    before = layer.counters().copy()
+    with pytest.raises(OttError, match="CAPACITY"):
+        layer.append(k[:, :, :1].contiguous(), k[:, :, :1].contiguous())
+    assert np.array_equal(layer.counters(), before)
+    assert layer.quantize_group() == 1
+    layer.append(k[:, :, :1].contiguous(), k[:, :, :1].contiguous())
+    assert layer.seq_state(0) == (161, 33, 128, 1)
+
+
+# ---- the five layer shapes ---------------------------------------------------
+def test_llama2_7b_full():
+    """32 heads, 4096 context, 64 steps with a quantize at step 32: every head."""
+    run_case(W["llama2-7b"])
+
+
+def test_llama2_7b_b32_sampled():
+    """Batch 32, ragged 3072-4096: sampled (sequence, head) pairs, all 64 steps."""
+    heads = [(0, 0), (5, 31), (13, 7), (21, 16), (30, 3), (31, 30)]
+    run_case(W["llama2-7b-b32"], heads=heads)
+
+
+def test_mistral_gqa_sampled():
+    run_case(W["mistral-7b-gqa"], heads=[(0, 0), (3, 5), (7, 7)], steps=6)
+
+
+def test_llama2_13b_128k_sampled():
+    run_case(W["llama2-13b-128k"], heads=[(0, 0), (0, 23), (0, 39)], steps=6)
