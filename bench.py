@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--workload", default="llama2-7b-b32")
     ap.add_argument("--states", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before warm-up, one device-to-device copy of this many MiB; its "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings calibrate the counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this OTT build has no multi-GPU path "
@@ -156,6 +159,14 @@ def main():
     del Kd, Vd
     torch.cuda.synchronize()
 
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     ones = [1] * w.batch

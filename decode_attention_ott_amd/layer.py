@@ -31,6 +31,8 @@ class OTTLayer:
         self.G, self.R, self.P = group_size, residual, pool_size
         self.max_seq_len = max_seq_len
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         need = L.ott_init(self.cfg, None, 0, sizing_only=True)
         self._buf = torch.empty(need + ALIGN, dtype=torch.uint8, device=self.device)
         off = (-self._buf.data_ptr()) % ALIGN
