@@ -118,6 +118,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="llama2-7b-b32")
     ap.add_argument("--states", type=int, default=3)
+    ap.add_argument("--splits", type=int, default=0, help="split-K factor (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before warm-up, one device-to-device copy of this many MiB; its "
@@ -146,6 +147,7 @@ def main():
     for i in range(args.states):
         lay = OTTLayer.for_workload(w, max_seq_len=n_pos)
         lay.prefill(Kd, Vd, lengths)
+        lay.set_num_splits(args.splits)
         layers.append(lay)
         print(f"[bench] state {i} prefilled", file=sys.stderr, flush=True)
     # per-state new tokens and queries, resident on the device
@@ -208,7 +210,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "decode_kernel<128>" + (" + combine_kernel" if False else ""),
+                "kernel": f"decode_kernel<{w.group_size}>",
                 "decode_us_mean": round(1e3 * sum(dec_ms) / len(dec_ms), 2),
                 "decode_us_median": round(1e3 * float(np.median(dec_ms)), 2),
                 "alg_bytes_per_launch": int(np.mean(alg_bytes))}
@@ -224,6 +226,7 @@ def main():
                       "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                       "context": f"{w.prefill[0]}-{w.prefill[1]}", "G": w.group_size,
                       "R": w.residual, "P": w.pool_size, "states": args.states,
+                      "splits": args.splits or "auto",
                       "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window"},
            "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)

@@ -44,10 +44,11 @@ ott_status_t validate_config(const ott_config_t* c) {
   return OTT_OK;
 }
 
+// Split-K capacity: enough partial slots for ~8K waves, 4..64 per head.
 int max_splits_for(const ott_config_t* c) {
   const int64_t heads = int64_t(c->batch) * c->num_kv_heads;
-  int64_t s = (1024 + heads - 1) / heads;
-  return int(std::max<int64_t>(1, std::min<int64_t>(64, s)));
+  const int64_t s = (8192 + heads - 1) / heads;
+  return int(std::max<int64_t>(4, std::min<int64_t>(64, s)));
 }
 
 void fill_layout(const ott_config_t* c, ott_layout_t* L) {
@@ -77,6 +78,7 @@ void fill_layout(const ott_config_t* c, ott_layout_t* L) {
   L->off_ring_k = take(BH * C * d * 2);
   L->off_ring_v = take(BH * C * d * 2);
   L->off_partials = take(B * Hq * uint64_t(L->max_splits) * (2 + d) * sizeof(float));
+  L->off_split_sync = take(B * Hq * sizeof(int32_t));
   L->arena_bytes = off;
 }
 
@@ -143,6 +145,7 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   a.off_ring_k = lay.off_ring_k;
   a.off_ring_v = lay.off_ring_v;
   a.off_partials = lay.off_partials;
+  a.off_split_sync = lay.off_split_sync;
   a.sm_scale = h->cfg.sm_scale;
   const size_t nb = size_t(cfg->batch);
   h->L.assign(nb, 0);
@@ -150,7 +153,9 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   h->head.assign(nb, 0);
   h->nb.assign(nb, 0);
   const size_t ctr_bytes = size_t(cfg->batch) * cfg->num_kv_heads * 4 * sizeof(int32_t);
-  if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess) {
+  const size_t sync_bytes = size_t(cfg->batch) * cfg->num_q_heads * sizeof(int32_t);
+  if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess ||
+      hipMemset(a.base + lay.off_split_sync, 0, sync_bytes) != hipSuccess) {
     delete h;
     return OTT_ERR_HIP;
   }
@@ -218,18 +223,20 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
   if (st != OTT_OK) return st;
   if (!d_q || !d_out) return OTT_ERR_INVALID_ARG;
   const int B = h->cfg.batch;
-  int units_max = 0;
+  // bytes of the largest head (pages + fp16 tokens) bound the useful split count
+  int64_t bytes_max = 0;
   for (int b = 0; b < B; ++b) {
     if (h->L[b] == 0) return OTT_ERR_STATE;
-    const int pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
-    const int units = h->nb[b] + (pc + h->rcnt[b] + ott::kFp16Chunk - 1) / ott::kFp16Chunk;
-    units_max = std::max(units_max, units);
+    const int64_t pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
+    bytes_max = std::max<int64_t>(bytes_max, int64_t(h->nb[b]) * int64_t(h->lay.page_bytes) +
+                                                 (pc + h->rcnt[b]) * 4 * h->cfg.head_dim);
   }
   int S = h->forced_splits;
   if (S <= 0) {
-    const int heads = B * h->cfg.num_kv_heads;
-    S = (heads >= 512) ? 1 : (1024 + heads - 1) / heads;
-    S = std::min(S, std::max(1, units_max / 4));
+    // about four work-groups per CU (1024), each with at least ~3 pages of work
+    const int64_t heads = int64_t(B) * h->cfg.num_kv_heads;
+    S = int((1024 + heads - 1) / heads);
+    S = int(std::min<int64_t>(S, std::max<int64_t>(1, bytes_max / (3 * int64_t(h->lay.page_bytes)))));
   }
   S = std::max(1, std::min(S, h->dev.max_splits));
   return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, static_cast<hipStream_t>(stream)));

@@ -19,7 +19,7 @@ struct Arena {
   uint32_t page_bytes;
   uint64_t off_counters, off_pages, off_page_pos, off_page_nvalid;
   uint64_t off_pool_k, off_pool_v, off_pool_pos, off_pool_n2;
-  uint64_t off_ring_k, off_ring_v, off_partials;
+  uint64_t off_ring_k, off_ring_v, off_partials, off_split_sync;
   float sm_scale;
 };
 

@@ -1,0 +1,352 @@
+// Cache-update kernels of the OTT path for gfx950 (CDNA4, wave64).
+//
+// Method: "Accurate KV Cache Quantization with Outlier Tokens Tracing"
+// (arXiv 2505.10938); [Blog] = zijie-tian.site summary page, [Abs] =
+// sciencestack.ai page (abstract and figure captions).
+//
+//   append_kernel    fp16 window update ([Blog] 3.3, residual window)
+//   quantize_kernel  quantization stage: Key norms, pool competition, 2-bit
+//                    pages ([Blog] 3.1, 3.2, flowchart; [Abs] Fig. 2 bottom)
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ott_device.h"
+
+namespace ott {
+namespace {
+using namespace dev;
+
+// ---------------------------------------------------------------------------
+// append
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __restrict__ k,
+                                                     const uint4* __restrict__ v,
+                                                     AppendCounts cnt) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int bh = b * a.Hkv + h;
+  const int n = cnt.uniform >= 0 ? cnt.uniform : int(cnt.n[b]);
+  if (n == 0) return;
+  int32_t* ctr = counters(a, bh);
+  const int r_cnt = ctr[1], head = ctr[2];
+  uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
+  uint4* rv = reinterpret_cast<uint4*>(ring_v(a, bh));
+  const size_t src = size_t(bh) * cnt.max_new * (D / 8);
+  for (int i = threadIdx.x; i < n * (D / 8); i += blockDim.x) {
+    const int t = i / (D / 8), c = i % (D / 8);
+    const int slot = (head + r_cnt + t) % a.C;
+    rk[size_t(slot) * (D / 8) + c] = k[src + i];
+    rv[size_t(slot) * (D / 8) + c] = v[src + i];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ctr[0] += n;
+    ctr[1] = r_cnt + n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quantize: one work-group per (sequence, KV head) with a full window
+// ---------------------------------------------------------------------------
+
+// 2-bit code of x against (min m, scale s): clamp(rint((x - m) / s), 0, 3).
+// x - m and the division are single IEEE fp32 operations (correctly rounded);
+// rintf rounds half to even.
+__device__ __forceinline__ uint32_t qcode(float x, float m, float s) {
+  if (s == 0.0f) return 0u;
+  const float y = __fdiv_rn(__fsub_rn(x, m), s);
+  const float r = fminf(fmaxf(rintf(y), 0.0f), 3.0f);
+  return uint32_t(r);
+}
+
+constexpr int kStageRows = 128;  // member rows staged in LDS at a time (32 KiB)
+
+struct QuantLds {
+  double* n2;
+  int* pos;
+  int* src;
+  int* rank;
+  int* mem;
+  float* kmin;
+  float* kscale;
+  float* vmin;
+  float* vscale;
+  __half* stage;  // [kStageRows][D]
+};
+
+__device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
+  QuantLds q;
+  q.stage = reinterpret_cast<__half*>(base);
+  q.n2 = reinterpret_cast<double*>(base + kStageRows * D * sizeof(__half));
+  q.pos = reinterpret_cast<int*>(q.n2 + NCmax);
+  q.src = q.pos + NCmax;
+  q.rank = q.src + NCmax;
+  q.mem = q.rank + NCmax;
+  q.kmin = reinterpret_cast<float*>(q.mem + G);
+  q.kscale = q.kmin + D;
+  q.vmin = q.kscale + D;
+  q.vscale = q.vmin + G;
+  return q;
+}
+
+// Copies rows [t0, t0+cnt) of the member list into the LDS stage with
+// independent 16-byte loads (one round trip for the whole chunk).
+template <typename RowFn>
+__device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, RowFn row) {
+  uint4* st = reinterpret_cast<uint4*>(s.stage);
+  for (int i = threadIdx.x; i < cnt * (D / 8); i += blockDim.x) {
+    const int t = i / (D / 8), c8 = i % (D / 8);
+    st[i] = reinterpret_cast<const uint4*>(row(s.src[s.mem[t0 + t]]))[c8];
+  }
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int bh = b * a.Hkv + h;
+  const int G = a.G, P = a.P, C = a.C;
+  int32_t* ctr = counters(a, bh);
+  const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
+  if (r_cnt < C) return;  // window not full: nothing to do for this sequence
+  const int tid = threadIdx.x;
+  const int pc = min(P, G * nb);  // pool tokens before this step
+  const int NC = pc + G;          // candidates: pool + group
+  const int npc = min(P, NC);     // pool tokens after this step
+  const int n_valid = NC - npc;   // page members
+  const int cur = nb & 1, nxt = cur ^ 1;
+  QuantLds s = quant_lds(lds_raw, P + G, G);
+
+  const __half* pk = pool_k(a, cur, bh);
+  const __half* pv = pool_v(a, cur, bh);
+  const __half* rk = ring_k(a, bh);
+  const __half* rv = ring_v(a, bh);
+  auto krow = [&](int src) -> const __half* {
+    return (src & kRingFlag) ? rk + size_t(src & ~kRingFlag) * D : pk + size_t(src) * D;
+  };
+  auto vrow = [&](int src) -> const __half* {
+    return (src & kRingFlag) ? rv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
+  };
+
+  // 1. candidates; squared Key norms of the group, fp64 in channel order
+  for (int i = tid; i < NC; i += blockDim.x) {
+    if (i < pc) {
+      s.n2[i] = pool_n2(a, cur, bh)[i];
+      s.pos[i] = pool_pos(a, cur, bh)[i];
+      s.src[i] = i;
+    } else {
+      const int j = i - pc;
+      const int slot = (head + j) % C;
+      const uint4* row = reinterpret_cast<const uint4*>(rk + size_t(slot) * D);
+      uint4 w[D / 8];
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) w[c8] = row[c8];
+      double acc = 0.0;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const uint32_t ws[4] = {w[c8].x, w[c8].y, w[c8].z, w[c8].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double lo = double(__half2float(__ushort_as_half(uint16_t(ws[e] & 0xffffu))));
+          const double hi = double(__half2float(__ushort_as_half(uint16_t(ws[e] >> 16))));
+          acc = acc + lo * lo;
+          acc = acc + hi * hi;
+        }
+      }
+      s.n2[i] = acc;
+      s.pos[i] = G * nb + j;
+      s.src[i] = slot | kRingFlag;
+    }
+  }
+  __syncthreads();
+
+  // 2. rank under (norm, position)
+  for (int i = tid; i < NC; i += blockDim.x) {
+    const double ni = s.n2[i];
+    const int pi = s.pos[i];
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < NC; ++j) {
+      const double nj = s.n2[j];
+      r += (nj < ni) || (nj == ni && s.pos[j] < pi);
+    }
+    s.rank[i] = r;
+  }
+  __syncthreads();
+
+  // 3. members (rank >= npc) in position order
+  for (int i = tid; i < NC; i += blockDim.x) {
+    if (s.rank[i] >= npc) {
+      const int pi = s.pos[i];
+      int idx = 0;
+#pragma unroll 8
+      for (int j = 0; j < NC; ++j) idx += (s.rank[j] >= npc) && (s.pos[j] < pi);
+      s.mem[idx] = i;
+    }
+  }
+  __syncthreads();
+
+  uint8_t* pg = page_ptr(a, bh, nb);
+  const int n_chunks = (n_valid + kStageRows - 1) / kStageRows;
+  // 4. Key (min, scale) per channel over the members
+  {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
+      stage_rows(s, t0, cnt, krow);
+      __syncthreads();
+      if (tid < D) {
+#pragma unroll 8
+        for (int t = 0; t < cnt; ++t) {
+          const float x = __half2float(s.stage[t * D + tid]);
+          lo = fminf(lo, x);
+          hi = fmaxf(hi, x);
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < D) {
+      if (n_valid == 0) lo = hi = 0.f;
+      const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
+      s.kmin[tid] = lo;
+      s.kscale[tid] = __half2float(sc);
+      const uint32_t word = uint32_t(__half_as_ushort(__float2half_rn(lo))) |
+                            (uint32_t(__half_as_ushort(sc)) << 16);
+      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = word;
+    }
+  }
+  __syncthreads();
+  // 5. K codes, token-major: dword (t, j) = channels 16j..16j+15 of member t
+  uint32_t* kc = reinterpret_cast<uint32_t*>(pg + kcode_off(G));
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
+    if (n_chunks > 1) {  // a single chunk is still staged from step 4
+      stage_rows(s, t0, cnt, krow);
+      __syncthreads();
+    }
+    const int jk = tid % (D / 16);  // this thread's 16 channels: 16*jk .. 16*jk+15
+    float km[16], ks[16];
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) {
+      km[cc] = s.kmin[16 * jk + cc];
+      ks[cc] = s.kscale[16 * jk + cc];
+    }
+    for (int w = tid; w < cnt * (D / 16); w += blockDim.x) {
+      const int t = w / (D / 16), j = jk;
+      const uint4* row = reinterpret_cast<const uint4*>(s.stage + t * D + 16 * j);
+      const uint4 r0 = row[0], r1 = row[1];
+      const uint32_t hw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        const uint16_t bits = uint16_t(cc & 1 ? hw[cc >> 1] >> 16 : hw[cc >> 1] & 0xffffu);
+        word |= qcode(__half2float(__ushort_as_half(bits)), km[cc], ks[cc]) << (2 * cc);
+      }
+      kc[(t0 + t) * (D / 16) + j] = word;
+    }
+    __syncthreads();
+  }
+  for (int w = n_valid * (D / 16) + tid; w < G * (D / 16); w += blockDim.x) kc[w] = 0u;
+
+  // 6. Values: per member (min, scale) over its channels, then V codes,
+  //    channel-major: dword (c, j) = slots 16j..16j+15 of channel c
+  uint32_t* vc = reinterpret_cast<uint32_t*>(pg + vcode_off(G));
+  uint32_t* vmeta = reinterpret_cast<uint32_t*>(pg + vmeta_off(G));
+  const int vdw = G / 16;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
+    stage_rows(s, t0, cnt, vrow);
+    __syncthreads();
+    if (tid < cnt) {
+      const __half* row = s.stage + tid * D;
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) {
+        const float x = __half2float(row[(i + 2 * tid) % D]);  // rotated: fewer bank conflicts
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+      const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+      s.vmin[t0 + tid] = mn;
+      s.vscale[t0 + tid] = __half2float(sc);
+      vmeta[t0 + tid] = uint32_t(__half_as_ushort(__float2half_rn(mn))) |
+                        (uint32_t(__half_as_ushort(sc)) << 16);
+    }
+    __syncthreads();
+    // dwords whose 16 slots start inside this chunk (chunks are multiples of 16)
+    const int jw0 = t0 / 16, jw1 = (t0 + cnt + 15) / 16;
+    for (int w = tid; w < D * (jw1 - jw0); w += blockDim.x) {
+      const int c = w % D, j = jw0 + w / D;
+      uint32_t word = 0;
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        const int t = 16 * j + cc;
+        if (t < n_valid)
+          word |= qcode(__half2float(s.stage[(t - t0) * D + c]), s.vmin[t], s.vscale[t]) << (2 * cc);
+      }
+      vc[c * vdw + j] = word;
+    }
+    __syncthreads();
+  }
+  for (int t = n_valid + tid; t < G; t += blockDim.x) vmeta[t] = 0u;
+  {
+    const int jfirst = (n_valid + 15) / 16;  // dwords holding no member
+    for (int w = tid; w < D * (vdw - jfirst); w += blockDim.x)
+      vc[(w / (vdw - jfirst)) * vdw + jfirst + w % (vdw - jfirst)] = 0u;
+  }
+  // 8. the new pool, slot = rank, into the other buffer
+  __half* nk = pool_k(a, nxt, bh);
+  __half* nv = pool_v(a, nxt, bh);
+  for (int w = tid; w < NC * (D / 8); w += blockDim.x) {
+    const int i = w / (D / 8), c8 = w % (D / 8);
+    const int r = s.rank[i];
+    if (r < npc) {
+      reinterpret_cast<uint4*>(nk + size_t(r) * D)[c8] =
+          reinterpret_cast<const uint4*>(krow(s.src[i]))[c8];
+      reinterpret_cast<uint4*>(nv + size_t(r) * D)[c8] =
+          reinterpret_cast<const uint4*>(vrow(s.src[i]))[c8];
+      if (c8 == 0) {
+        pool_pos(a, nxt, bh)[r] = s.pos[i];
+        pool_n2(a, nxt, bh)[r] = s.n2[i];
+      }
+    }
+  }
+  // 9. member positions (tests only)
+  int32_t* ppos = reinterpret_cast<int32_t*>(a.base + a.off_page_pos) +
+                  (size_t(bh) * a.nb_max + nb) * G;
+  for (int t = tid; t < G; t += blockDim.x) ppos[t] = t < n_valid ? s.pos[s.mem[t]] : -1;
+  if (tid == 0)
+    reinterpret_cast<int32_t*>(a.base + a.off_page_nvalid)[size_t(bh) * a.nb_max + nb] = n_valid;
+  __syncthreads();
+  if (tid == 0) {
+    ctr[1] = r_cnt - G;
+    ctr[2] = (head + G) % C;
+    ctr[3] = nb + 1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const Arena& a, const void* k, const void* v, const AppendCounts& n,
+                         hipStream_t s) {
+  dim3 grid(a.Hkv, a.B);
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, a, static_cast<const uint4*>(k),
+                     static_cast<const uint4*>(v), n);
+  return hipGetLastError();
+}
+
+size_t quantize_lds_bytes(int G, int P) {
+  using dev::D;
+  const size_t nc = size_t(P) + G;
+  return size_t(kStageRows) * D * 2 + nc * sizeof(double) + 3 * nc * sizeof(int) +
+         G * sizeof(int) + 2 * D * sizeof(float) + 2 * size_t(G) * sizeof(float);
+}
+
+hipError_t launch_quantize(const Arena& a, hipStream_t s) {
+  dim3 grid(a.Hkv, a.B);
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), quantize_lds_bytes(a.G, a.P), s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ott

@@ -86,7 +86,8 @@ typedef struct {
  *              its first min(P, G*nb) slots are used, ascending (norm, position).
  *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
  *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
- *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states.
+ *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}.
+ *   split_sync int32 [B][Hq]: arrival counters of the split-K merge; zero between calls.
  */
 typedef struct {
   uint64_t arena_bytes;
@@ -106,14 +107,16 @@ typedef struct {
   uint64_t off_ring_k;
   uint64_t off_ring_v;
   uint64_t off_partials;
+  uint64_t off_split_sync;
 } ott_layout_t;
 
 /*
  * ott_init - validate a config, size the arena, and create a handle.
  *   Sizing: pass d_arena = NULL and out = NULL; *required_bytes receives the size.
  *   Create: pass a device arena of >= required bytes (256-byte aligned); *out
- *   receives the handle. The per-(sequence, head) counters are zeroed with a
- *   blocking hipMemset on the default stream; nothing else is touched.
+ *   receives the handle. The per-(sequence, head) counters and the split-K
+ *   arrival counters are zeroed with blocking hipMemset calls on the default
+ *   stream; nothing else is touched.
  *   required_bytes may be NULL when creating.
  */
 ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes,

@@ -49,11 +49,11 @@ def test_sizing_matches_layout_formula():
     al = lambda x: (x + 255) // 256 * 256
     page = G * d // 4 * 2 + 4 * d + 4 * G
     assert page == 9216
-    S = min(64, (1024 + B * Hkv - 1) // (B * Hkv))
+    S = max(4, min(64, (8192 + B * Hkv - 1) // (B * Hkv)))
     want = (al(B * Hkv * 16) + al(B * Hkv * NB * page) + al(B * Hkv * NB * G * 4)
             + al(B * Hkv * NB * 4) + 2 * al(2 * B * Hkv * P * d * 2) + al(2 * B * Hkv * P * 4)
             + al(2 * B * Hkv * P * 8) + 2 * al(B * Hkv * (R + G) * d * 2)
-            + al(B * Hq * S * (2 + d) * 4))
+            + al(B * Hq * S * (2 + d) * 4) + al(B * Hq * 4))
     assert req == want
 
 
