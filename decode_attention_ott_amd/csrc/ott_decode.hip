@@ -83,12 +83,11 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 __device__ __forceinline__ float pair_sum(float x) { return x + dpp<kQuadSwap1>(x); }
 
-// Orders this wave's LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Orders this wave's LDS writes before its later LDS reads. A wave's LDS
+// instructions execute in issue order, so only the compiler must be kept from
+// moving them; a memory fence here would also wait for every outstanding
+// global load (the next page's codes included).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ float lo_f(uint32_t w) {
   return __half2float(__ushort_as_half(uint16_t(w & 0xffffu)));
@@ -165,6 +164,21 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// Streaming (non-temporal) loads: each cached byte is read once per decode.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_nt2(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld_nt4(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_nt1(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+}
+
 // 2^x with one v_exp_f32 (denormal results flush to zero: such softmax
 // weights are below 2^-126 of the running maximum and do not matter).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -223,35 +237,35 @@ struct PageRegs {
   static constexpr int VW = G / 64;       // V dwords per lane and channel (>= 1)
   uint2 kc[KP];
   uint32_t vc[8][VW];
-  uint32_t vm[KP];
+  uint32_t vm[KP / 4];  // V (min, scale) of this lane's tokens 16(4i+j)+ti
   uint2 km;
 };
 
+// Loads in the order the page is consumed (K meta, K codes, V meta, V codes)
+// so that each wait only covers what the next step needs.
 template <int G>
 __device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ pg,
                                           int lane) {
   constexpr int KP = PageRegs<G>::KP, VW = PageRegs<G>::VW;
   const int j = lane & 3, ti = lane >> 2;
+  r.km = ld_nt2(pg + kmeta_off(G) + 8 * lane);
 #pragma unroll
-  for (int k = 0; k < KP; ++k)
-    r.kc[k] = *reinterpret_cast<const uint2*>(pg + (16 * k + ti) * (D / 4) + 8 * j);
+  for (int k = 0; k < KP; ++k) r.kc[k] = ld_nt2(pg + (16 * k + ti) * (D / 4) + 8 * j);
+#pragma unroll
+  for (int i = 0; i < KP / 4; ++i) r.vm[i] = ld_nt1(pg + vmeta_off(G) + 4 * (16 * (4 * i + j) + ti));
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint8_t* src = pg + vcode_off(G) + (16 * k + ti) * (G / 4) + j * (G / 16);
     if constexpr (VW == 4) {
-      const uint4 t = *reinterpret_cast<const uint4*>(src);
+      const uint4 t = ld_nt4(src);
       r.vc[k][0] = t.x; r.vc[k][1] = t.y; r.vc[k][2] = t.z; r.vc[k][3] = t.w;
     } else if constexpr (VW == 2) {
-      const uint2 t = *reinterpret_cast<const uint2*>(src);
+      const uint2 t = ld_nt2(src);
       r.vc[k][0] = t.x; r.vc[k][1] = t.y;
     } else {
-      r.vc[k][0] = *reinterpret_cast<const uint32_t*>(src);
+      r.vc[k][0] = ld_nt1(src);
     }
   }
-#pragma unroll
-  for (int k = 0; k < KP; ++k)
-    r.vm[k] = reinterpret_cast<const uint32_t*>(pg + vmeta_off(G))[16 * k + ti];
-  r.km = reinterpret_cast<const uint2*>(pg + kmeta_off(G))[lane];
 }
 
 template <int G>
@@ -277,28 +291,40 @@ __device__ __forceinline__ void compute_page(const PageRegs<G>& r, int n_valid, 
     for (int k = 0; k < KP; ++k)
       z[k] = dot16_codes(h ? r.kc[k].y : r.kc[k].x, c0, c1, c2, c3, z[k]);
   }
-  float mx = -INFINITY;
+  // transpose-reduce inside the quad: afterwards lane j holds the full score
+  // of tokens 16(4i+j)+ti, i = 0..KP/4-1
+  constexpr int KT = KP / 4;
+  float za[KP / 2];
 #pragma unroll
-  for (int k = 0; k < KP; ++k) z[k] = quad_sum(z[k]) + bias;
+  for (int i = 0; i < KP / 2; ++i) {
+    const float keep = (j & 1) ? z[2 * i + 1] : z[2 * i];
+    const float send = (j & 1) ? z[2 * i] : z[2 * i + 1];
+    za[i] = keep + dpp<kQuadSwap1>(send);
+  }
+  float zt[KT];
+#pragma unroll
+  for (int i = 0; i < KT; ++i) {
+    const float keep = (j & 2) ? za[2 * i + 1] : za[2 * i];
+    const float send = (j & 2) ? za[2 * i] : za[2 * i + 1];
+    zt[i] = keep + dpp<kQuadSwap2>(send) + bias;
+  }
   if (n_valid < G) {  // only a page built while the pool was filling is short
 #pragma unroll
-    for (int k = 0; k < KP; ++k)
-      if (16 * k + ti >= n_valid) z[k] = -INFINITY;
+    for (int i = 0; i < KT; ++i)
+      if (16 * (4 * i + j) + ti >= n_valid) zt[i] = -INFINITY;
   }
+  float mx = zt[0];
 #pragma unroll
-  for (int k = 0; k < KP; ++k) mx = fmaxf(mx, z[k]);
+  for (int i = 1; i < KT; ++i) mx = fmaxf(mx, zt[i]);
   mx = wave_max(mx);
   if (mx == -INFINITY) return;  // a page without members
   rescale_q(st, fmaxf(st.m, mx));
 #pragma unroll
-  for (int k = 0; k < KP; ++k) {
-    const float p = exp2_fast(z[k] - st.m);
-    if (j == 0) {
-      const int t = 16 * k + ti;
-      st.l += p;
-      st.vmin = fmaf(p, lo_f(r.vm[k]), st.vmin);
-      ph[pair_slot(t)] = _Float16(2.0f * p * hi_f(r.vm[k]));
-    }
+  for (int i = 0; i < KT; ++i) {
+    const float p = exp2_fast(zt[i] - st.m);
+    st.l += p;
+    st.vmin = fmaf(p, lo_f(r.vm[i]), st.vmin);
+    ph[pair_slot(16 * (4 * i + j) + ti)] = _Float16(2.0f * p * hi_f(r.vm[i]));
   }
   wave_lds_sync();
 #pragma unroll
@@ -324,25 +350,28 @@ struct Fp16Src {
   const __half* rv;
   int pc, head, C;
   __device__ __forceinline__ size_t row(int i) const {
-    return i < pc ? size_t(i) * D : size_t((head + i - pc) % C) * D;
+    if (i < pc) return size_t(i) * D;
+    const int x = head + i - pc;  // < 2C: head < C and i - pc < r_cnt <= C
+    return size_t(x >= C ? x - C : x) * D;
   }
   __device__ __forceinline__ const __half* k(int i) const { return (i < pc ? pk : rk) + row(i); }
   __device__ __forceinline__ const __half* v(int i) const { return (i < pc ? pv : rv) + row(i); }
 };
 
-constexpr int kF16Pass = 8;                 // 4 tokens per pass
+constexpr int kF16Pass = 4;                 // 4 tokens per pass
 constexpr int kF16Chunk = 4 * kF16Pass;     // tokens per chunk
 
 __device__ __forceinline__ void fp16_chunk(const Fp16Src& src, int base, int cnt, const uint4& q8,
                                            float qscale, Fp16State& st, int lane) {
   const int rw = lane >> 4, c8 = lane & 15;
   float z[kF16Pass];
-  uint4 kv[kF16Pass];
+  uint4 kv[kF16Pass], vv[kF16Pass];
   // rows past the chunk read the chunk's last token (in bounds); their
-  // weights are forced to zero below
+  // weights are forced to zero below. K and V rows are requested together.
 #pragma unroll
-  for (int p = 0; p < kF16Pass; ++p)
-    kv[p] = reinterpret_cast<const uint4*>(src.k(base + min(4 * p + rw, cnt - 1)))[c8];
+  for (int p = 0; p < kF16Pass; ++p) kv[p] = ld_nt4(src.k(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
+#pragma unroll
+  for (int p = 0; p < kF16Pass; ++p) vv[p] = ld_nt4(src.v(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
   float mx = -INFINITY;
 #pragma unroll
   for (int p = 0; p < kF16Pass; ++p) {
@@ -365,15 +394,14 @@ __device__ __forceinline__ void fp16_chunk(const Fp16Src& src, int base, int cnt
   for (int p = 0; p < kF16Pass; ++p) {
     const float w = exp2_fast(z[p] - st.m);
     lsum += w;
-    const uint4 vv = reinterpret_cast<const uint4*>(src.v(base + min(4 * p + rw, cnt - 1)))[c8];
-    st.acc[0] = fmaf(w, lo_f(vv.x), st.acc[0]);
-    st.acc[1] = fmaf(w, hi_f(vv.x), st.acc[1]);
-    st.acc[2] = fmaf(w, lo_f(vv.y), st.acc[2]);
-    st.acc[3] = fmaf(w, hi_f(vv.y), st.acc[3]);
-    st.acc[4] = fmaf(w, lo_f(vv.z), st.acc[4]);
-    st.acc[5] = fmaf(w, hi_f(vv.z), st.acc[5]);
-    st.acc[6] = fmaf(w, lo_f(vv.w), st.acc[6]);
-    st.acc[7] = fmaf(w, hi_f(vv.w), st.acc[7]);
+    st.acc[0] = fmaf(w, lo_f(vv[p].x), st.acc[0]);
+    st.acc[1] = fmaf(w, hi_f(vv[p].x), st.acc[1]);
+    st.acc[2] = fmaf(w, lo_f(vv[p].y), st.acc[2]);
+    st.acc[3] = fmaf(w, hi_f(vv[p].y), st.acc[3]);
+    st.acc[4] = fmaf(w, lo_f(vv[p].z), st.acc[4]);
+    st.acc[5] = fmaf(w, hi_f(vv[p].z), st.acc[5]);
+    st.acc[6] = fmaf(w, lo_f(vv[p].w), st.acc[6]);
+    st.acc[7] = fmaf(w, hi_f(vv[p].w), st.acc[7]);
   }
   if (c8 == 0) st.l += lsum;  // each row's tokens counted once
 }
@@ -435,36 +463,48 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
     if (qi < NQ) {
       const int qh = h * NQ + qi;
       const __half* qrow = q + (size_t(b) * a.Hq + qh) * D;
+      const uint32_t q2 = reinterpret_cast<const uint32_t*>(qrow)[lane];
+      const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
+      const float qs0 = lo_f(q2) * qscale, qs1 = hi_f(q2) * qscale;
       WaveState st;
-      {
-        // fp16 tokens first: this wave's 32-token chunks
+      st.m = -INFINITY;
+      st.l = 0.f;
+      st.vmin = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) st.acc[k] = 0.f;
+      // fp16 chunks (memory-heavy) are spread between pages (compute-heavy),
+      // staggered by wave, so the work-group always mixes the two
+      int chunk = t0 + stripe * kF16Chunk;
+      auto next_chunk = [&]() {
         Fp16State fs;
         fs.m = -INFINITY;
         fs.l = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) fs.acc[k] = 0.f;
-        const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
-        for (int base = t0 + stripe * kF16Chunk; base < t1; base += wph * kF16Chunk)
-          fp16_chunk(src, base, min(kF16Chunk, t1 - base), q8, qscale, fs, lane);
-        // fold into the page layout (channel 16k + lane/4, quarter lane&3)
+        fp16_chunk(src, chunk, min(kF16Chunk, t1 - chunk), q8, qscale, fs, lane);
+        chunk += wph * kF16Chunk;
+        // fold (m, l, acc) of the chunk into the page state; acc changes
+        // layout through LDS (channel 8*(lane&15)+e, row lane>>4 -> quad layout)
+        const float M = fmaxf(st.m, fs.m);
+        rescale_q(st, M);
+        const float af = (fs.m == -INFINITY) ? 0.f : exp2_fast(fs.m - M);
+        st.l = fmaf(fs.l, af, st.l);
         float4* f = reinterpret_cast<float4*>(&L.fin[lane >> 4][8 * (lane & 15)]);
-        f[0] = make_float4(fs.acc[0], fs.acc[1], fs.acc[2], fs.acc[3]);
-        f[1] = make_float4(fs.acc[4], fs.acc[5], fs.acc[6], fs.acc[7]);
+        f[0] = make_float4(fs.acc[0] * af, fs.acc[1] * af, fs.acc[2] * af, fs.acc[3] * af);
+        f[1] = make_float4(fs.acc[4] * af, fs.acc[5] * af, fs.acc[6] * af, fs.acc[7] * af);
         wave_lds_sync();
 #pragma unroll
-        for (int k = 0; k < 8; ++k) st.acc[k] = L.fin[lane & 3][16 * k + (lane >> 2)];
+        for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
         wave_lds_sync();
-        st.m = fs.m;
-        st.l = fs.l;
-        st.vmin = 0.f;
-      }
-      const uint32_t q2 = reinterpret_cast<const uint32_t*>(qrow)[lane];
-      const float qs0 = lo_f(q2) * qscale, qs1 = hi_f(q2) * qscale;
-      for (int u = p0 + stripe; u < p1; u += wph) {
+      };
+      int n = 0;
+      for (int u = p0 + stripe; u < p1; u += wph, ++n) {
         PageRegs<G> pr;
         load_page<G>(pr, pages + size_t(u) * PB, lane);
         compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
+        if ((n & 3) == (stripe & 3) && chunk < t1) next_chunk();
       }
+      while (chunk < t1) next_chunk();
 
       // this wave's state -> LDS in channel order
       const float l_tot = wave_sum(st.l);
