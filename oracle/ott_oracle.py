@@ -28,7 +28,7 @@ What the pages fix, and what this module does:
     takes one softmax, multiplies by each kind of Value and sums ([Blog]
     flowchart; [Abs] Fig. 2 top).
 
-Readings where the pages are silent (each one listed in the design doc):
+Readings taken where the pages are silent:
   R1  outlier = the P smallest squared L2 Key norms; no channel test.
   R2  squared norm = fp64 sum of exact squares in channel order 0..d-1;
       ties broken by lower position.
