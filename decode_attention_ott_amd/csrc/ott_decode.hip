@@ -19,91 +19,17 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "ott_device.h"
+#include "ott_decode_common.h"
 
 namespace ott {
 namespace {
 using namespace dev;
-
-constexpr int kWaves = 4;           // waves (work items) per work-group
-constexpr int kFp16TokenBytes = 4 * D;  // K + V bytes of one fp16 token
-
-// ---------------------------------------------------------------------------
-// cross-lane helpers (DPP inside 16-lane rows, permlane swaps across rows)
-// ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-// every lane of a 16-lane row receives the row's sum / max
-__device__ __forceinline__ float row_sum(float x) {
-  x += dpp<kQuadSwap1>(x);
-  x += dpp<kQuadSwap2>(x);
-  x += dpp<kHalfMirror>(x);
-  x += dpp<kRowMirror>(x);
-  return x;
-}
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp<kQuadSwap1>(x));
-  x = fmaxf(x, dpp<kQuadSwap2>(x));
-  x = fmaxf(x, dpp<kHalfMirror>(x));
-  x = fmaxf(x, dpp<kRowMirror>(x));
-  return x;
-}
-// combine each lane with its partner row (lane ^ 16) / partner half (lane ^ 32)
-__device__ __forceinline__ f32x2 swap16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return f32x2{__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1]))};
-}
-__device__ __forceinline__ f32x2 swap32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return f32x2{__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1]))};
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row_sum(x);
-  f32x2 p = swap16(x);
-  x = p.x + p.y;
-  p = swap32(x);
-  return p.x + p.y;
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = row_max(x);
-  f32x2 p = swap16(x);
-  x = fmaxf(p.x, p.y);
-  p = swap32(x);
-  return fmaxf(p.x, p.y);
-}
-__device__ __forceinline__ float pair_sum(float x) { return x + dpp<kQuadSwap1>(x); }
-
-// Orders this wave's LDS writes before its later LDS reads. A wave's LDS
-// instructions execute in issue order, so only the compiler must be kept from
-// moving them; a memory fence here would also wait for every outstanding
-// global load (the next page's codes included).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory"); }
-
-__device__ __forceinline__ float lo_f(uint32_t w) {
-  return __half2float(__ushort_as_half(uint16_t(w & 0xffffu)));
-}
-__device__ __forceinline__ float hi_f(uint32_t w) {
-  return __half2float(__ushort_as_half(uint16_t(w >> 16)));
-}
-__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
-                                false);
-}
+using namespace dec;
 
 // Dot of 16 2-bit codes (one dword, code i in bits 2i..2i+1) with 16 weights.
 // A nibble whose two high bits are zero is the FP4 (E2M1) value code/2, so two
 // masks turn the dword into 8 + 8 FP4 values and each byte converts to two
-// floats in one instruction. Weights must be pre-doubled.
+// floats in one instruction, so the result is half the true dot product.
 __device__ __forceinline__ float dot16_codes(uint32_t w, const float4& c0, const float4& c1,
                                              const float4& c2, const float4& c3, float acc) {
   const uint32_t ev = w & 0x33333333u;         // codes 0 and 2 of every byte
@@ -139,7 +65,7 @@ __device__ __forceinline__ float dot16_codes(uint32_t w, const float4& c0, const
 // Same for 16 codes against fp16 weights held as pairs per group of 4 slots:
 // group g gives {(w[4g], w[4g+2]), (w[4g+1], w[4g+3])}, the order in which the
 // FP4 -> f16 conversion returns codes (0,2) and (1,3) of a byte; pa holds
-// groups 0 and 1 of the dword, pb groups 2 and 3. Weights pre-doubled.
+// groups 0 and 1 of the dword, pb groups 2 and 3. Half the true dot product.
 __device__ __forceinline__ float dot16_codes_h(uint32_t w, const uint4& pa, const uint4& pb,
                                                float acc) {
   const uint32_t ev = w & 0x33333333u;
@@ -160,53 +86,14 @@ __device__ __forceinline__ int pair_slot(int s) {
   return (s & ~3) | ((s & 1) << 1) | ((s >> 1) & 1);
 }
 
-__device__ __forceinline__ uint32_t dw(const uint4& v, int j) {
-  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// Streaming (non-temporal) loads: each cached byte is read once per decode.
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 ld_nt2(const void* p) {
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
-}
-__device__ __forceinline__ uint4 ld_nt4(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t ld_nt1(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
-}
-
-// 2^x with one v_exp_f32 (denormal results flush to zero: such softmax
-// weights are below 2^-126 of the running maximum and do not matter).
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Online softmax state of one wave (scores in log2 units) while it walks
 // quantized pages.
 struct WaveState {
   float m;        // running max (wave-uniform)
   float l;        // this lane's share of the running sum of weights
   float vmin;     // this lane's share of sum p_t * min_t over quantized tokens
-  float acc[8];   // channel 16k + lane/4, slot quarter lane&3
+  float acc[8];   // channel 16k + lane/4, slot quarter lane&3; half units
 };
-// The same while it walks fp16 tokens (done first, then folded into WaveState).
-struct Fp16State {
-  float m;
-  float l;
-  float acc[8];   // channels 8*(lane&15) .. +7, tokens of row lane>>4
-};
-
-template <int N, typename St>
-__device__ __forceinline__ void rescale(St& st, float m_new) {
-  if (m_new == st.m) return;  // wave-uniform: the running max did not move
-  const float alpha = (st.m == -INFINITY) ? 0.f : exp2_fast(st.m - m_new);
-  st.m = m_new;
-  st.l *= alpha;
-#pragma unroll
-  for (int k = 0; k < N; ++k) st.acc[k] *= alpha;
-}
 __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
   if (m_new == st.m) return;
   const float alpha = (st.m == -INFINITY) ? 0.f : exp2_fast(st.m - m_new);
@@ -215,12 +102,6 @@ __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
   st.vmin *= alpha;
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.acc[k] *= alpha;
-}
-
-__device__ __forceinline__ float quad_sum(float x) {
-  x += dpp<kQuadSwap1>(x);
-  x += dpp<kQuadSwap2>(x);
-  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -324,7 +205,8 @@ __device__ __forceinline__ void compute_page(const PageRegs<G>& r, int n_valid, 
     const float p = exp2_fast(zt[i] - st.m);
     st.l += p;
     st.vmin = fmaf(p, lo_f(r.vm[i]), st.vmin);
-    ph[pair_slot(16 * (4 * i + j) + ti)] = _Float16(2.0f * p * hi_f(r.vm[i]));
+    // p' = p * scale_t stays below 2^16 (p <= 1, scale <= 2^16 / 3) in fp16
+    ph[pair_slot(16 * (4 * i + j) + ti)] = _Float16(p * hi_f(r.vm[i]));
   }
   wave_lds_sync();
 #pragma unroll
@@ -338,81 +220,11 @@ __device__ __forceinline__ void compute_page(const PageRegs<G>& r, int n_valid, 
 }
 
 // ---------------------------------------------------------------------------
-// fp16 tokens: the pool (index i < pc) then the window (ring slot (head+i-pc)%C)
+// the kernel (one query head per KV head)
 // ---------------------------------------------------------------------------
-// 16 lanes share one token (lane&15 takes channels 8*(lane&15)..+7), so every
-// load instruction reads 4 whole 256-byte rows. Scores reduce inside the row
-// with DPP; the row then holds the token's weight for its V accumulation.
-struct Fp16Src {
-  const __half* pk;
-  const __half* pv;
-  const __half* rk;
-  const __half* rv;
-  int pc, head, C;
-  __device__ __forceinline__ size_t row(int i) const {
-    if (i < pc) return size_t(i) * D;
-    const int x = head + i - pc;  // < 2C: head < C and i - pc < r_cnt <= C
-    return size_t(x >= C ? x - C : x) * D;
-  }
-  __device__ __forceinline__ const __half* k(int i) const { return (i < pc ? pk : rk) + row(i); }
-  __device__ __forceinline__ const __half* v(int i) const { return (i < pc ? pv : rv) + row(i); }
-};
-
-constexpr int kF16Pass = 4;                 // 4 tokens per pass
-constexpr int kF16Chunk = 4 * kF16Pass;     // tokens per chunk
-
-__device__ __forceinline__ void fp16_chunk(const Fp16Src& src, int base, int cnt, const uint4& q8,
-                                           float qscale, Fp16State& st, int lane) {
-  const int rw = lane >> 4, c8 = lane & 15;
-  float z[kF16Pass];
-  uint4 kv[kF16Pass], vv[kF16Pass];
-  // rows past the chunk read the chunk's last token (in bounds); their
-  // weights are forced to zero below. K and V rows are requested together.
-#pragma unroll
-  for (int p = 0; p < kF16Pass; ++p) kv[p] = ld_nt4(src.k(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
-#pragma unroll
-  for (int p = 0; p < kF16Pass; ++p) vv[p] = ld_nt4(src.v(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < kF16Pass; ++p) {
-    float acc = fdot2(kv[p].x, q8.x, 0.f);
-    acc = fdot2(kv[p].y, q8.y, acc);
-    acc = fdot2(kv[p].z, q8.z, acc);
-    acc = fdot2(kv[p].w, q8.w, acc);
-    z[p] = (4 * p + rw < cnt) ? row_sum(acc) * qscale : -INFINITY;
-    mx = fmaxf(mx, z[p]);
-  }
-  {
-    f32x2 pm = swap16(mx);
-    mx = fmaxf(pm.x, pm.y);
-    pm = swap32(mx);
-    mx = fmaxf(pm.x, pm.y);
-  }
-  rescale<8>(st, fmaxf(st.m, mx));
-  float lsum = 0.f;
-#pragma unroll
-  for (int p = 0; p < kF16Pass; ++p) {
-    const float w = exp2_fast(z[p] - st.m);
-    lsum += w;
-    st.acc[0] = fmaf(w, lo_f(vv[p].x), st.acc[0]);
-    st.acc[1] = fmaf(w, hi_f(vv[p].x), st.acc[1]);
-    st.acc[2] = fmaf(w, lo_f(vv[p].y), st.acc[2]);
-    st.acc[3] = fmaf(w, hi_f(vv[p].y), st.acc[3]);
-    st.acc[4] = fmaf(w, lo_f(vv[p].z), st.acc[4]);
-    st.acc[5] = fmaf(w, hi_f(vv[p].z), st.acc[5]);
-    st.acc[6] = fmaf(w, lo_f(vv[p].w), st.acc[6]);
-    st.acc[7] = fmaf(w, hi_f(vv[p].w), st.acc[7]);
-  }
-  if (c8 == 0) st.l += lsum;  // each row's tokens counted once
-}
-
-// ---------------------------------------------------------------------------
-// the kernel
-// ---------------------------------------------------------------------------
-// Work-group = 4 waves on one (sequence, KV head, split). With one query head
-// per KV head the 4 waves share the split (pages and 32-token chunks dealt
-// round-robin) and merge in LDS; with a query-head group every wave takes its
-// own query head(s) over the whole split.
+// Work-group = 4 waves on one (sequence, head, split). The waves deal the
+// split's pages round-robin, spread the fp16 chunks between their pages and
+// merge their states in LDS.
 struct alignas(16) WaveLds {
   float qp[D];          // q' of the current page
   _Float16 ph[256];     // p' of the current page, pair layout (G <= 256)
@@ -428,127 +240,105 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   WaveLds& L = lds_all[wave];
-  const int NQ = a.Hq / a.Hkv;
   const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;
-  const int b = bh / a.Hkv, h = bh % a.Hkv;
+  const int bh = blockIdx.x / S;  // = b * H + h, also the query head's index
+  const int b = bh / a.Hkv;
 
   const int32_t* ctr = counters(a, bh);
   const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
   const int pc = min(a.P, a.G * nb);
-  const int n16 = pc + r_cnt;
-  // byte-balanced split: pages first, then fp16 tokens
-  const int64_t PB = a.page_bytes;
-  const int64_t W = nb * PB + int64_t(n16) * kFp16TokenBytes;
-  const int64_t lo = int64_t(s) * W / S, hi = int64_t(s + 1) * W / S;
-  auto first_page = [&](int64_t x) { return int(min<int64_t>(nb, (x + PB - 1) / PB)); };
-  auto first_tok = [&](int64_t x) {
-    const int64_t r = x - nb * PB;
-    return r <= 0 ? 0 : int(min<int64_t>(n16, (r + kFp16TokenBytes - 1) / kFp16TokenBytes));
-  };
-  const int p0 = first_page(lo), p1 = first_page(hi);
-  const int t0 = first_tok(lo), t1 = first_tok(hi);
+  const Split sp = split_of(nb, pc + r_cnt, a.page_bytes, s, S);
+  const int p1 = sp.p1, t1 = sp.t1;
   const int buf = nb & 1;
   const Fp16Src src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
                     head, a.C};
   const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
+  const int64_t PB = a.page_bytes;
 
-  const int wph = NQ >= kWaves ? 1 : kWaves / NQ;  // waves per query head
-  const int hpr = kWaves / wph;                    // query heads per round
-  const int rounds = (NQ + hpr - 1) / hpr;
-  for (int r = 0; r < rounds; ++r) {
-    const int qi = r * hpr + wave / wph;
-    const int stripe = wave % wph;
-    if (qi < NQ) {
-      const int qh = h * NQ + qi;
-      const __half* qrow = q + (size_t(b) * a.Hq + qh) * D;
-      const uint32_t q2 = reinterpret_cast<const uint32_t*>(qrow)[lane];
-      const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
-      const float qs0 = lo_f(q2) * qscale, qs1 = hi_f(q2) * qscale;
-      WaveState st;
-      st.m = -INFINITY;
-      st.l = 0.f;
-      st.vmin = 0.f;
+  const __half* qrow = q + size_t(bh) * D;
+  const uint32_t q2 = reinterpret_cast<const uint32_t*>(qrow)[lane];
+  const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
+  const float qs0 = lo_f(q2) * qscale, qs1 = hi_f(q2) * qscale;
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.vmin = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) st.acc[k] = 0.f;
-      // fp16 chunks (memory-heavy) are spread between pages (compute-heavy),
-      // staggered by wave, so the work-group always mixes the two
-      int chunk = t0 + stripe * kF16Chunk;
-      auto next_chunk = [&]() {
-        Fp16State fs;
-        fs.m = -INFINITY;
-        fs.l = 0.f;
+  for (int k = 0; k < 8; ++k) st.acc[k] = 0.f;
+  // fp16 chunks (memory-heavy) are spread between pages (compute-heavy),
+  // staggered by wave, so the work-group always mixes the two
+  int chunk = sp.t0 + wave * kF16Chunk;
+  auto next_chunk = [&]() {
+    Fp16State fs;
+    fs.m = -INFINITY;
+    fs.l = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) fs.acc[k] = 0.f;
-        fp16_chunk(src, chunk, min(kF16Chunk, t1 - chunk), q8, qscale, fs, lane);
-        chunk += wph * kF16Chunk;
-        // fold (m, l, acc) of the chunk into the page state; acc changes
-        // layout through LDS (channel 8*(lane&15)+e, row lane>>4 -> quad layout)
-        const float M = fmaxf(st.m, fs.m);
-        rescale_q(st, M);
-        const float af = (fs.m == -INFINITY) ? 0.f : exp2_fast(fs.m - M);
-        st.l = fmaf(fs.l, af, st.l);
-        float4* f = reinterpret_cast<float4*>(&L.fin[lane >> 4][8 * (lane & 15)]);
-        f[0] = make_float4(fs.acc[0] * af, fs.acc[1] * af, fs.acc[2] * af, fs.acc[3] * af);
-        f[1] = make_float4(fs.acc[4] * af, fs.acc[5] * af, fs.acc[6] * af, fs.acc[7] * af);
-        wave_lds_sync();
+    for (int k = 0; k < 8; ++k) fs.acc[k] = 0.f;
+    fp16_chunk(src, chunk, min(kF16Chunk, t1 - chunk), q8, qscale, fs, lane);
+    chunk += kWaves * kF16Chunk;
+    // fold (m, l, acc) of the chunk into the page state; acc changes layout
+    // through LDS (channel 8*(lane&15)+e, row lane>>4 -> quad layout) and
+    // enters in half units
+    const float M = fmaxf(st.m, fs.m);
+    rescale_q(st, M);
+    const float af = (fs.m == -INFINITY) ? 0.f : exp2_fast(fs.m - M);
+    st.l = fmaf(fs.l, af, st.l);
+    const float ah = 0.5f * af;
+    float4* f = reinterpret_cast<float4*>(&L.fin[lane >> 4][8 * (lane & 15)]);
+    f[0] = make_float4(fs.acc[0] * ah, fs.acc[1] * ah, fs.acc[2] * ah, fs.acc[3] * ah);
+    f[1] = make_float4(fs.acc[4] * ah, fs.acc[5] * ah, fs.acc[6] * ah, fs.acc[7] * ah);
+    wave_lds_sync();
 #pragma unroll
-        for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
-        wave_lds_sync();
-      };
-      int n = 0;
-      for (int u = p0 + stripe; u < p1; u += wph, ++n) {
-        PageRegs<G> pr;
-        load_page<G>(pr, pages + size_t(u) * PB, lane);
-        compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
-        if ((n & 3) == (stripe & 3) && chunk < t1) next_chunk();
-      }
-      while (chunk < t1) next_chunk();
+    for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
+    wave_lds_sync();
+  };
+  int n = 0;
+  for (int u = sp.p0 + wave; u < p1; u += kWaves, ++n) {
+    PageRegs<G> pr;
+    load_page<G>(pr, pages + size_t(u) * PB, lane);
+    compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
+    if ((n & 3) == wave && chunk < t1) next_chunk();
+  }
+  while (chunk < t1) next_chunk();
 
-      // this wave's state -> LDS in channel order
-      const float l_tot = wave_sum(st.l);
-      const float v_tot = wave_sum(st.vmin);
+  // this wave's state -> LDS in channel order (accumulator back to full units)
+  const float l_tot = wave_sum(st.l);
+  const float v_tot = wave_sum(st.vmin);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) st.acc[k] = quad_sum(st.acc[k]);
-      if ((lane & 3) == 0) {
+  for (int k = 0; k < 8; ++k) st.acc[k] = quad_sum(st.acc[k]);
+  if ((lane & 3) == 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) L.fin[0][16 * k + (lane >> 2)] = st.acc[k] + v_tot;
-      }
-      if (lane == 0) {
-        mg_m[wave] = st.m;
-        mg_l[wave] = l_tot;
+    for (int k = 0; k < 8; ++k) L.fin[0][16 * k + (lane >> 2)] = fmaf(2.0f, st.acc[k], v_tot);
+  }
+  if (lane == 0) {
+    mg_m[wave] = st.m;
+    mg_l[wave] = l_tot;
+  }
+  __syncthreads();
+  // merge the 4 waves
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mg_m[w]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = (mg_m[w] == -INFINITY) ? 0.f : exp2f(mg_m[w] - M);
+      Ls = fmaf(mg_l[w], f, Ls);
+      A = fmaf(lds_all[w].fin[0][c], f, A);
+    }
+    if (S == 1) {
+      out[size_t(bh) * D + c] = __float2half_rn(A / Ls);
+    } else {
+      float* part = partial_ptr(a, b, bh % a.Hq, s);
+      part[2 + c] = A;
+      if (c == 0) {
+        part[0] = M;
+        part[1] = Ls;
       }
     }
-    __syncthreads();
-    // merge the waves of each query head of this round
-    for (int jx = threadIdx.x; jx < hpr * D; jx += blockDim.x) {
-      const int hr = jx / D, c = jx % D;
-      const int qi2 = r * hpr + hr;
-      if (qi2 >= NQ) continue;
-      float M = -INFINITY;
-      for (int w = hr * wph; w < (hr + 1) * wph; ++w) M = fmaxf(M, mg_m[w]);
-      float Ls = 0.f, A = 0.f;
-      for (int w = hr * wph; w < (hr + 1) * wph; ++w) {
-        const float f = (mg_m[w] == -INFINITY) ? 0.f : exp2f(mg_m[w] - M);
-        const float aw = lds_all[w].fin[0][c];
-        Ls = fmaf(mg_l[w], f, Ls);
-        A = fmaf(aw, f, A);
-      }
-      const int qh = h * NQ + qi2;
-      if (S == 1) {
-        out[(size_t(b) * a.Hq + qh) * D + c] = __float2half_rn(A / Ls);
-      } else {
-        float* part = reinterpret_cast<float*>(a.base + a.off_partials) +
-                      ((size_t(b) * a.Hq + qh) * a.max_splits + s) * (2 + D);
-        part[2 + c] = A;
-        if (c == 0) {
-          part[0] = M;
-          part[1] = Ls;
-        }
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -573,16 +363,21 @@ __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict_
 }  // namespace
 
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, hipStream_t s) {
-  const dim3 grid(unsigned(a.B) * a.Hkv * S);
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);
-  switch (a.G) {
-    case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
-    case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
-    case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
-    default: return hipErrorInvalidValue;
+  hipError_t e;
+  if (a.Hq != a.Hkv) {
+    e = launch_decode_gqa(a, q, out, S, s);
+  } else {
+    const dim3 grid(unsigned(a.B) * a.Hkv * S);
+    switch (a.G) {
+      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
+      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
+      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(a.B) * a.Hq), dim3(D), 0, s, a, oh, S);
   return hipGetLastError();

@@ -1,0 +1,251 @@
+// Device helpers shared by the decode kernels (gfx950, wave64): cross-lane
+// reductions, streaming loads, the online-softmax rescale and the fp16-token
+// (outlier pool + recent window) chunk walker.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ott_device.h"
+
+namespace ott {
+namespace dec {
+using namespace dev;
+
+constexpr int kWaves = 4;           // waves (work items) per work-group
+constexpr int kFp16TokenBytes = 4 * D;  // K + V bytes of one fp16 token
+
+// ---------------------------------------------------------------------------
+// cross-lane helpers (DPP inside 16-lane rows, permlane swaps across rows)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// every lane of a 16-lane row receives the row's sum / max
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  return x;
+}
+// combine each lane with its partner row (lane ^ 16) / partner half (lane ^ 32)
+__device__ __forceinline__ f32x2 swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return f32x2{__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1]))};
+}
+__device__ __forceinline__ f32x2 swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return f32x2{__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1]))};
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum(x);
+  f32x2 p = swap16(x);
+  x = p.x + p.y;
+  p = swap32(x);
+  return p.x + p.y;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max(x);
+  f32x2 p = swap16(x);
+  x = fmaxf(p.x, p.y);
+  p = swap32(x);
+  return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float pair_sum(float x) { return x + dpp<kQuadSwap1>(x); }
+
+// Orders this wave's LDS writes before its later LDS reads. A wave's LDS
+// instructions execute in issue order, so only the compiler must be kept from
+// moving them; a memory fence here would also wait for every outstanding
+// global load (the next page's codes included).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ float lo_f(uint32_t w) {
+  return __half2float(__ushort_as_half(uint16_t(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_f(uint32_t w) {
+  return __half2float(__ushort_as_half(uint16_t(w >> 16)));
+}
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                false);
+}
+
+// dword j (0..3) of a 16-byte vector
+__device__ __forceinline__ uint32_t dw(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Streaming (non-temporal) loads: each cached byte is read once per decode.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_nt2(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld_nt4(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_nt1(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p));
+}
+
+// 2^x with one v_exp_f32 (denormal results flush to zero: such softmax
+// weights are below 2^-126 of the running maximum and do not matter).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online softmax state (scores in log2 units) of one wave over fp16 tokens;
+// a kernel folds it into its page state.
+struct Fp16State {
+  float m;
+  float l;
+  float acc[8];   // channels 8*(lane&15) .. +7, tokens of row lane>>4
+};
+
+template <int N, typename St>
+__device__ __forceinline__ void rescale(St& st, float m_new) {
+  if (m_new == st.m) return;  // wave-uniform: the running max did not move
+  const float alpha = (st.m == -INFINITY) ? 0.f : exp2_fast(st.m - m_new);
+  st.m = m_new;
+  st.l *= alpha;
+#pragma unroll
+  for (int k = 0; k < N; ++k) st.acc[k] *= alpha;
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 tokens: the pool (index i < pc) then the window (ring slot (head+i-pc)%C)
+// ---------------------------------------------------------------------------
+// 16 lanes share one token (lane&15 takes channels 8*(lane&15)..+7), so every
+// load instruction reads 4 whole 256-byte rows. Scores reduce inside the row
+// with DPP; the row then holds the token's weight for its V accumulation.
+struct Fp16Src {
+  const __half* pk;
+  const __half* pv;
+  const __half* rk;
+  const __half* rv;
+  int pc, head, C;
+  __device__ __forceinline__ size_t row(int i) const {
+    if (i < pc) return size_t(i) * D;
+    const int x = head + i - pc;  // < 2C: head < C and i - pc < r_cnt <= C
+    return size_t(x >= C ? x - C : x) * D;
+  }
+  __device__ __forceinline__ const __half* k(int i) const { return (i < pc ? pk : rk) + row(i); }
+  __device__ __forceinline__ const __half* v(int i) const { return (i < pc ? pv : rv) + row(i); }
+};
+
+constexpr int kF16Pass = 4;                 // 4 tokens per pass
+constexpr int kF16Chunk = 4 * kF16Pass;     // tokens per chunk
+
+// The K and V rows of one chunk as this lane holds them.
+struct Fp16Rows {
+  uint4 k[kF16Pass], v[kF16Pass];
+};
+
+__device__ __forceinline__ void fp16_load(const Fp16Src& src, int base, int cnt, Fp16Rows& r,
+                                          int lane) {
+  const int rw = lane >> 4, c8 = lane & 15;
+  // rows past the chunk read the chunk's last token (in bounds); their
+  // weights are forced to zero. K and V rows are requested together.
+#pragma unroll
+  for (int p = 0; p < kF16Pass; ++p) r.k[p] = ld_nt4(src.k(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
+#pragma unroll
+  for (int p = 0; p < kF16Pass; ++p) r.v[p] = ld_nt4(src.v(base + min(4 * p + rw, cnt - 1)) + 8 * c8);
+}
+
+// One query against a loaded chunk of cnt tokens, folded into st.
+__device__ __forceinline__ void fp16_attend(const Fp16Rows& r, int cnt, const uint4& q8,
+                                            float qscale, Fp16State& st, int lane) {
+  const int rw = lane >> 4, c8 = lane & 15;
+  float z[kF16Pass];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kF16Pass; ++p) {
+    float acc = fdot2(r.k[p].x, q8.x, 0.f);
+    acc = fdot2(r.k[p].y, q8.y, acc);
+    acc = fdot2(r.k[p].z, q8.z, acc);
+    acc = fdot2(r.k[p].w, q8.w, acc);
+    z[p] = (4 * p + rw < cnt) ? row_sum(acc) * qscale : -INFINITY;
+    mx = fmaxf(mx, z[p]);
+  }
+  {
+    f32x2 pm = swap16(mx);
+    mx = fmaxf(pm.x, pm.y);
+    pm = swap32(mx);
+    mx = fmaxf(pm.x, pm.y);
+  }
+  rescale<8>(st, fmaxf(st.m, mx));
+  float lsum = 0.f;
+#pragma unroll
+  for (int p = 0; p < kF16Pass; ++p) {
+    const float w = exp2_fast(z[p] - st.m);
+    lsum += w;
+    st.acc[0] = fmaf(w, lo_f(r.v[p].x), st.acc[0]);
+    st.acc[1] = fmaf(w, hi_f(r.v[p].x), st.acc[1]);
+    st.acc[2] = fmaf(w, lo_f(r.v[p].y), st.acc[2]);
+    st.acc[3] = fmaf(w, hi_f(r.v[p].y), st.acc[3]);
+    st.acc[4] = fmaf(w, lo_f(r.v[p].z), st.acc[4]);
+    st.acc[5] = fmaf(w, hi_f(r.v[p].z), st.acc[5]);
+    st.acc[6] = fmaf(w, lo_f(r.v[p].w), st.acc[6]);
+    st.acc[7] = fmaf(w, hi_f(r.v[p].w), st.acc[7]);
+  }
+  if (c8 == 0) st.l += lsum;  // each row's tokens counted once
+}
+
+__device__ __forceinline__ void fp16_chunk(const Fp16Src& src, int base, int cnt, const uint4& q8,
+                                           float qscale, Fp16State& st, int lane) {
+  Fp16Rows r;
+  fp16_load(src, base, cnt, r, lane);
+  fp16_attend(r, cnt, q8, qscale, st, lane);
+}
+
+// Byte-balanced split of one (sequence, KV head)'s cache: split s of S takes
+// the pages [p0, p1) and the fp16 tokens [t0, t1) whose bytes fall in the
+// s-th S-th of the head's bytes (pages first, then fp16 tokens).
+struct Split {
+  int p0, p1, t0, t1;
+};
+__device__ __forceinline__ Split split_of(int nb, int n16, int64_t PB, int s, int S) {
+  const int64_t W = nb * PB + int64_t(n16) * kFp16TokenBytes;
+  const int64_t lo = int64_t(s) * W / S, hi = int64_t(s + 1) * W / S;
+  auto first_page = [&](int64_t x) { return int(min<int64_t>(nb, (x + PB - 1) / PB)); };
+  auto first_tok = [&](int64_t x) {
+    const int64_t r = x - nb * PB;
+    return r <= 0 ? 0 : int(min<int64_t>(n16, (r + kFp16TokenBytes - 1) / kFp16TokenBytes));
+  };
+  return Split{first_page(lo), first_page(hi), first_tok(lo), first_tok(hi)};
+}
+
+// Partial state of split s for (sequence b, query head qh): {m, l, acc[D]}.
+__device__ __forceinline__ float* partial_ptr(const Arena& a, int b, int qh, int s) {
+  return reinterpret_cast<float*>(a.base + a.off_partials) +
+         ((size_t(b) * a.Hq + qh) * a.max_splits + s) * (2 + D);
+}
+
+}  // namespace dec
+}  // namespace ott

@@ -34,6 +34,10 @@ hipError_t launch_append(const Arena& a, const void* k, const void* v, const App
                          hipStream_t s);
 hipError_t launch_quantize(const Arena& a, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits, hipStream_t s);
+// The decode kernel for a group of query heads per KV head (Hq > Hkv); it
+// writes the output (one split) or the split partials like launch_decode.
+hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int num_splits,
+                             hipStream_t s);
 
 // Dynamic LDS bytes the quantize kernel needs for (G, P).
 size_t quantize_lds_bytes(int G, int P);

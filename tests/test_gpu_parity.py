@@ -45,9 +45,34 @@ def test_parameters(G, R, P, L, steps):
              state_every_step=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2), (12, 3)])
+# query-head groups of 2, 4, 8, 16 and 32 (two passes of 16) per KV head
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2), (12, 3), (32, 2), (64, 2)])
 def test_grouped_query_heads(Hq, Hkv):
     run_case(small(f"gqa{Hq}x{Hkv}", Hq=Hq, Hkv=Hkv, L=(520, 520), steps=6, seed=Hq))
+
+
+@pytest.mark.parametrize("G,R,P,L,Hq", [
+    (64, 16, 8, (300, 300), 8),       # G=64
+    (256, 64, 128, (700, 700), 8),    # G=256 with a large pool
+    (256, 64, 128, (700, 700), 32),   # G=256, 16 heads per pass
+    (64, 16, 8, (300, 300), 32),      # G=64, 16 heads per pass
+    (128, 32, 160, (600, 600), 8),    # P > G: first page has no members
+    (128, 32, 0, (500, 500), 4),      # P=0
+])
+def test_grouped_query_parameters(G, R, P, L, Hq):
+    run_case(small(f"gqa-g{G}r{R}p{P}h{Hq}", Hq=Hq, G=G, R=R, P=P, L=L, steps=4, seed=3 * G + P),
+             state_every_step=True)
+
+
+def test_grouped_query_split_counts_agree():
+    w = small("gqa-splits", B=2, Hq=8, Hkv=2, L=(2000, 2000), steps=2)
+    run_case(w, splits=[1, 2, 3, 7, 16, 0])
+
+
+def test_grouped_query_huge_keys():
+    """Outlier channels x8000 and queries x16: |q * scale| per channel exceeds
+    the fp16 range, so the page's query operand is scaled down first."""
+    run_case(small("gqa-hugek", Hq=8, L=(700, 700), steps=3, chan_scale=8000.0), q_scale=16.0)
 
 
 def test_ragged_and_short_sequences():
