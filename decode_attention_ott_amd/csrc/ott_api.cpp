@@ -16,6 +16,7 @@ struct ott_ctx {
   ott::Arena dev;
   std::vector<int32_t> L, rcnt, head, nb;  // identical for every KV head of a sequence
   int32_t forced_splits = 0;
+  int64_t slots = 1024;  // decode work-groups the GPU holds at once
   bool poisoned = false;
 };
 
@@ -154,6 +155,17 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   h->nb.assign(nb, 0);
   const size_t ctr_bytes = size_t(cfg->batch) * cfg->num_kv_heads * 4 * sizeof(int32_t);
   const size_t sync_bytes = size_t(cfg->batch) * cfg->num_q_heads * sizeof(int32_t);
+  {
+    // one round of decode work-groups fills the GPU: CUs x work-groups per CU
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    int wpc = ott::decode_wgs_per_cu(a);
+    if (wpc <= 0) wpc = 4;
+    h->slots = int64_t(cus) * wpc;
+  }
   if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess ||
       hipMemset(a.base + lay.off_split_sync, 0, sync_bytes) != hipSuccess) {
     delete h;
@@ -233,9 +245,10 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
   }
   int S = h->forced_splits;
   if (S <= 0) {
-    // about four work-groups per CU (1024), each with at least ~3 pages of work
+    // as many work-groups as the GPU holds at once, each with at least ~3
+    // pages of work
     const int64_t heads = int64_t(B) * h->cfg.num_kv_heads;
-    S = int((1024 + heads - 1) / heads);
+    S = int(std::max<int64_t>(1, h->slots / heads));
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, bytes_max / (3 * int64_t(h->lay.page_bytes)))));
   }
   S = std::max(1, std::min(S, h->dev.max_splits));

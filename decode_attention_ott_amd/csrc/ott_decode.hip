@@ -362,6 +362,19 @@ __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict_
 
 }  // namespace
 
+int decode_wgs_per_cu(const Arena& a) {
+  if (a.Hq != a.Hkv) return decode_gqa_wgs_per_cu(a);
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (a.G) {
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<64>, 64 * kWaves, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<128>, 64 * kWaves, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<256>, 64 * kWaves, 0); break;
+    default: break;
+  }
+  return e == hipSuccess ? n : 0;
+}
+
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);

@@ -582,7 +582,29 @@ hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, hipStre
   return hipGetLastError();
 }
 
+template <int G>
+int wgs_g(const Arena& a) {
+  const int NQ = a.Hq / a.Hkv;
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  const int bs = 64 * kWaves;
+  if (NQ % 16 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 16>, bs, 0);
+  else if (NQ % 8 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 8>, bs, 0);
+  else if (NQ % 4 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 4>, bs, 0);
+  else if (NQ == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 2>, bs, 0);
+  return e == hipSuccess ? n : 0;
+}
+
 }  // namespace
+
+int decode_gqa_wgs_per_cu(const Arena& a) {
+  switch (a.G) {
+    case 64: return wgs_g<64>(a);
+    case 128: return wgs_g<128>(a);
+    case 256: return wgs_g<256>(a);
+    default: return 0;
+  }
+}
 
 hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int S, hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);

@@ -38,6 +38,10 @@ hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_split
 // writes the output (one split) or the split partials like launch_decode.
 hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int num_splits,
                              hipStream_t s);
+// Work-groups of the decode kernel this arena's shape launches that fit on
+// one CU at once (0 if the runtime cannot tell).
+int decode_wgs_per_cu(const Arena& a);
+int decode_gqa_wgs_per_cu(const Arena& a);
 
 // Dynamic LDS bytes the quantize kernel needs for (G, P).
 size_t quantize_lds_bytes(int G, int P);

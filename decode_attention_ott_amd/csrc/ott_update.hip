@@ -51,43 +51,55 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
 // quantize: one work-group per (sequence, KV head) with a full window
 // ---------------------------------------------------------------------------
 
-// 2-bit code of x against (min m, scale s): clamp(rint((x - m) / s), 0, 3).
-// x - m and the division are single IEEE fp32 operations (correctly rounded);
-// rintf rounds half to even.
-__device__ __forceinline__ uint32_t qcode(float x, float m, float s) {
-  if (s == 0.0f) return 0u;
-  const float y = __fdiv_rn(__fsub_rn(x, m), s);
-  const float r = fminf(fmaxf(rintf(y), 0.0f), 3.0f);
-  return uint32_t(r);
+// 2-bit code of x against (min m, scale s): clamp(rint(y), 0, 3) with
+// y = fl32(fl32(x - m) / s), rint rounding half to even, computed without a
+// division. The code counts the rounding thresholds y passes: y > 0.5,
+// y >= 1.5, y > 2.5. With d = fl32(x - m) and q = d / s exact:
+//   fl32(q) > 0.5  <=>  q > 0.5 + 2^-25  (the midpoint to the next float rounds
+//                                        to the even 0.5)
+//   fl32(q) >= 1.5 <=>  q >= 1.5 - 2^-24 (the midpoint below rounds up to 1.5)
+//   fl32(q) > 2.5  <=>  q > 2.5 + 2^-23  (the midpoint above rounds down)
+// For an fp16 scale, 0.5 s, 1.5 s and 2.5 s are exact in fp32, and no fp32 d
+// lies strictly between c s and c s (1 +- 2^-24) (the float spacing there is
+// wider), so the tests are d > 0.5 s, d >= 1.5 s, d > 2.5 s in fp32. A zero
+// scale gives code 0 (thresholds +inf).
+struct CodeThr {
+  float m, t1, t2, t3;
+};
+
+__device__ __forceinline__ CodeThr code_thresholds(float m, float s) {
+  if (!(s > 0.0f)) return CodeThr{m, INFINITY, INFINITY, INFINITY};
+  return CodeThr{m, 0.5f * s, 1.5f * s, 2.5f * s};
+}
+
+__device__ __forceinline__ uint32_t qcode(float x, const CodeThr& q) {
+  const float d = __fsub_rn(x, q.m);
+  return uint32_t(d > q.t1) + uint32_t(d >= q.t2) + uint32_t(d > q.t3);
 }
 
 constexpr int kStageRows = 128;  // member rows staged in LDS at a time (32 KiB)
 
 struct QuantLds {
+  __half* stage;  // [kStageRows][D]
+  CodeThr* kq;    // [D] per channel: K min and code thresholds
+  CodeThr* vq;    // [G] per member: V min and code thresholds
   double* n2;
   int* pos;
   int* src;
   int* rank;
   int* mem;
-  float* kmin;
-  float* kscale;
-  float* vmin;
-  float* vscale;
-  __half* stage;  // [kStageRows][D]
 };
 
 __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
   QuantLds q;
   q.stage = reinterpret_cast<__half*>(base);
-  q.n2 = reinterpret_cast<double*>(base + kStageRows * D * sizeof(__half));
+  q.kq = reinterpret_cast<CodeThr*>(base + kStageRows * D * sizeof(__half));
+  q.vq = q.kq + D;
+  q.n2 = reinterpret_cast<double*>(q.vq + G);
   q.pos = reinterpret_cast<int*>(q.n2 + NCmax);
   q.src = q.pos + NCmax;
   q.rank = q.src + NCmax;
   q.mem = q.rank + NCmax;
-  q.kmin = reinterpret_cast<float*>(q.mem + G);
-  q.kscale = q.kmin + D;
-  q.vmin = q.kscale + D;
-  q.vscale = q.vmin + G;
   return q;
 }
 
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
   }
   __syncthreads();
 
-  // 2. rank under (norm, position)
+  // 2. rank under (norm, position); branch-free so the LDS reads pipeline
   for (int i = tid; i < NC; i += blockDim.x) {
     const double ni = s.n2[i];
     const int pi = s.pos[i];
@@ -169,7 +181,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
 #pragma unroll 8
     for (int j = 0; j < NC; ++j) {
       const double nj = s.n2[j];
-      r += (nj < ni) || (nj == ni && s.pos[j] < pi);
+      const int pj = s.pos[j];
+      r += int(nj < ni) | (int(nj == ni) & int(pj < pi));
     }
     s.rank[i] = r;
   }
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
       const int pi = s.pos[i];
       int idx = 0;
 #pragma unroll 8
-      for (int j = 0; j < NC; ++j) idx += (s.rank[j] >= npc) && (s.pos[j] < pi);
+      for (int j = 0; j < NC; ++j) idx += int(s.rank[j] >= npc) & int(s.pos[j] < pi);
       s.mem[idx] = i;
     }
   }
@@ -209,8 +222,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
     if (tid < D) {
       if (n_valid == 0) lo = hi = 0.f;
       const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
-      s.kmin[tid] = lo;
-      s.kscale[tid] = __half2float(sc);
+      s.kq[tid] = code_thresholds(lo, __half2float(sc));
       const uint32_t word = uint32_t(__half_as_ushort(__float2half_rn(lo))) |
                             (uint32_t(__half_as_ushort(sc)) << 16);
       reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = word;
@@ -226,12 +238,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
       __syncthreads();
     }
     const int jk = tid % (D / 16);  // this thread's 16 channels: 16*jk .. 16*jk+15
-    float km[16], ks[16];
+    CodeThr kq[16];
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
-      km[cc] = s.kmin[16 * jk + cc];
-      ks[cc] = s.kscale[16 * jk + cc];
-    }
+    for (int cc = 0; cc < 16; ++cc) kq[cc] = s.kq[16 * jk + cc];
     for (int w = tid; w < cnt * (D / 16); w += blockDim.x) {
       const int t = w / (D / 16), j = jk;
       const uint4* row = reinterpret_cast<const uint4*>(s.stage + t * D + 16 * j);
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
 #pragma unroll
       for (int cc = 0; cc < 16; ++cc) {
         const uint16_t bits = uint16_t(cc & 1 ? hw[cc >> 1] >> 16 : hw[cc >> 1] & 0xffffu);
-        word |= qcode(__half2float(__ushort_as_half(bits)), km[cc], ks[cc]) << (2 * cc);
+        word |= qcode(__half2float(__ushort_as_half(bits)), kq[cc]) << (2 * cc);
       }
       kc[(t0 + t) * (D / 16) + j] = word;
     }
@@ -268,8 +277,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
         mx = fmaxf(mx, x);
       }
       const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
-      s.vmin[t0 + tid] = mn;
-      s.vscale[t0 + tid] = __half2float(sc);
+      s.vq[t0 + tid] = code_thresholds(mn, __half2float(sc));
       vmeta[t0 + tid] = uint32_t(__half_as_ushort(__float2half_rn(mn))) |
                         (uint32_t(__half_as_ushort(sc)) << 16);
     }
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
       for (int cc = 0; cc < 16; ++cc) {
         const int t = 16 * j + cc;
         if (t < n_valid)
-          word |= qcode(__half2float(s.stage[(t - t0) * D + c]), s.vmin[t], s.vscale[t]) << (2 * cc);
+          word |= qcode(__half2float(s.stage[(t - t0) * D + c]), s.vq[t]) << (2 * cc);
       }
       vc[c * vdw + j] = word;
     }
@@ -339,8 +347,8 @@ hipError_t launch_append(const Arena& a, const void* k, const void* v, const App
 size_t quantize_lds_bytes(int G, int P) {
   using dev::D;
   const size_t nc = size_t(P) + G;
-  return size_t(kStageRows) * D * 2 + nc * sizeof(double) + 3 * nc * sizeof(int) +
-         G * sizeof(int) + 2 * D * sizeof(float) + 2 * size_t(G) * sizeof(float);
+  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) + nc * sizeof(double) +
+         3 * nc * sizeof(int) + G * sizeof(int);
 }
 
 hipError_t launch_quantize(const Arena& a, hipStream_t s) {
