@@ -11,10 +11,10 @@
 //   values  o[h][c] += sum_t p'[h][t] * vcode[c][t]            (QB x G x 128)
 //
 // with q'[h][c] = qs[h][c] * scale_c and p'[h][t] = p[h][t] * scale_t. Both
-// run on v_mfma_f32_16x16x32_f16. A 2-bit code c enters as the fp16 value
-// 1 + c/4 (exponent of 1.0, the code in the two top mantissa bits: one and-or
-// per two codes); the constant part is folded into the bias of the scores and
-// into the min term of the values. q' enters as an fp16 pair hi + lo (22
+// run on v_mfma_f32_16x16x32_f16. A 2-bit code whose two high neighbour bits
+// are masked off is the FP4 (E2M1) value code/2, which one conversion per two
+// codes turns into fp16 (0, 0.5, 1, 1.5: exact and normal); the factor 2
+// returns after the products. q' enters as an fp16 pair hi + lo (22
 // significant bits), p' as one fp16 value.
 #include "ott_decode_common.h"
 
@@ -35,38 +35,34 @@ __device__ __forceinline__ f4 mfma16(const h8& a, const h8& b, const f4& c) {
 }
 
 // One dword of 16 codes (code n in bits 2n..2n+1) as the B operands of two
-// MFMA steps: slot e of step h holds 1 + c/4 for code c = 4h + (e >> 1) +
-// 8 (e & 1) (the code lands in mantissa bits 8..9 of the half). `one` holds
-// 0x3C003C00 (1.0 in both halves) in a vector register, so that each output
-// dword is a single v_and_or_b32.
-__device__ __forceinline__ void codes_b(uint32_t w, uint32_t one, h8& b0, h8& b1) {
-  constexpr uint32_t M = 0x03000300u;
-  u4v x, y;
-  x[0] = ((w << 8) & M) | one;
-  x[1] = ((w << 6) & M) | one;
-  x[2] = ((w << 4) & M) | one;
-  x[3] = ((w << 2) & M) | one;
-  y[0] = (w & M) | one;
-  y[1] = ((w >> 2) & M) | one;
-  y[2] = ((w >> 4) & M) | one;
-  y[3] = ((w >> 6) & M) | one;
-  b0 = __builtin_bit_cast(h8, x);
-  b1 = __builtin_bit_cast(h8, y);
+// MFMA steps, as code/2: slot e of step h holds code 8h + kPerm[e] (each FP4
+// conversion yields codes 0 and 2, or 1 and 3, of one byte).
+__device__ __forceinline__ void codes_b(uint32_t w, h8& b0, h8& b1) {
+  const uint32_t ev = w & 0x33333333u;         // codes 0 and 2 of every byte
+  const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1 and 3 of every byte
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0);
+  const h2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0);
+  const h2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1);
+  const h2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1);
+  const h2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2);
+  const h2 o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2);
+  const h2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3);
+  const h2 o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3);
+  b0 = h8{e0[0], e0[1], o0[0], o0[1], e1[0], e1[1], o1[0], o1[1]};
+  b1 = h8{e2[0], e2[1], o2[0], o2[1], e3[0], e3[1], o3[0], o3[1]};
 }
 
-__device__ __forceinline__ uint32_t ones_f16x2() {
-  uint32_t one;
-  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(one));
-  return one;
-}
+// Code (channel or token) offset of slot e inside an MFMA step.
+__host__ __device__ constexpr int kPerm(int e) { return (e & ~3) | ((e & 1) << 1) | ((e >> 1) & 1); }
 
 // Shapes for page size G and QB query heads per pass.
 //   K: tile T = tokens 16T..16T+15 (B column = token); lane group g covers
 //      channels 32g..32g+31 of the token's code row, step cb the channels
-//      32g + 16(cb>>1) + 4(cb&1) + {0..3, 8..11}.
+//      32g + 8cb + kPerm(slot).
 //   V: tile ct = channels 16ct..16ct+15 (B column = channel); lane group g
 //      covers tokens g*G/4..g*G/4+G/4-1 of the channel's code row, step kb the
-//      tokens g*G/4 + 16(kb>>1) + 4(kb&1) + {0..3, 8..11}.
+//      tokens g*G/4 + 8kb + kPerm(slot).
 //   A rows: query head h at row h (its q' hi part and p'), q' lo part at row
 //      QB + h; with QB = 16 the lo parts fill a second 16-row array.
 template <int G, int QB>
@@ -76,7 +72,7 @@ struct Geo {
   static constexpr int KT = G / 16;                 // K tiles
   static constexpr int VDW = G / 64;                // V code dwords per lane and channel
   static constexpr int KB = G / 32;                 // V steps
-  static constexpr int NP = G / 2;                  // token pairs (t, t + 8)
+  static constexpr int NP = G / 2;                  // token pairs (t, t + 2)
   static constexpr int PPL = (NP + 63) / 64;        // pairs per lane
   static constexpr int QPL = (QB + 3) / 4;          // query heads per lane in the q' step
   static constexpr int ZS0 = G * ZR > 4 * D ? G * ZR : 4 * D;
@@ -87,12 +83,12 @@ struct Geo {
   static constexpr int NBLK = NA * 16 > KB * 4 ? NA * 16 : KB * 4;
 };
 
-// First token of pair pi; the pair is (t, t + 8) and fills the dword p of
-// A row h in V step kb for lane group g.
+// First token of pair pi; the pair is (t, t + 2) and fills the dword p (slots
+// 2p, 2p + 1) of A row h in V step kb for lane group g.
 template <int G>
 __device__ __forceinline__ int pair_token(int pi) {
   const int g = pi / (G / 8), rem = pi % (G / 8), kb = rem >> 2, p = rem & 3;
-  return g * (G / 4) + 16 * (kb >> 1) + 4 * (kb & 1) + p;
+  return g * (G / 4) + 8 * kb + (p & 1) + 4 * (p >> 1);
 }
 
 template <int G, int QB>
@@ -110,8 +106,8 @@ template <int QB>
 struct GqaState {
   float m[QB];     // running max per query head (wave-uniform)
   float l[QB];     // this lane's share of the running sums
-  float vmin[QB];  // this lane's share of sum p_t * min_t - 4 sum p'_t
-  f4 acc[8];       // sum p'_t (1 + c_t/4): rows 4(lane>>4)+r, channel 16ct + (lane&15)
+  float vmin[QB];  // this lane's share of sum p_t * min_t
+  f4 acc[8];       // sum p'_t c_t / 2: rows 4(lane>>4)+r, channel 16ct + (lane&15)
 };
 
 // Per-lane value of a per-head array for D row 4g + r.
@@ -151,7 +147,7 @@ __device__ __forceinline__ void wave_max_n(float (&x)[N]) {
 template <int G>
 struct GqaPage {
   static constexpr int KT = G / 16, VDW = G / 64, PPL = (G / 2 + 63) / 64;
-  uint4 kmA, kmB;        // K (min, scale) of the lane's q' channels
+  uint4 kmA, kmB;        // K (min, scale) of the lane's q' channels 8j..8j+7
   uint2 kc[KT];          // K codes: tile T, token 16T + (lane&15), lane group's 32 channels
   uint32_t vm[PPL][2];   // V (min, scale) of the lane's token pairs
   uint32_t vc[8][VDW];   // V codes: tile ct, channel 16ct + (lane&15), lane group's tokens
@@ -161,17 +157,16 @@ template <int G>
 __device__ __forceinline__ void gqa_load(GqaPage<G>& r, const uint8_t* __restrict__ pg, int lane) {
   constexpr int NP = G / 2;
   const int j = lane & 15, g = lane >> 4;
-  const int cg = j >> 2, cb = j & 3;  // q' chunk of this lane: lane group cg, step cb
-  const int c0 = 32 * cg + 16 * (cb >> 1) + 4 * (cb & 1);
+  const int c0 = 8 * j;  // q' chunk of this lane: channels c0..c0+7 (lane group j>>2, step j&3)
   r.kmA = ld_nt4(pg + kmeta_off(G) + 4 * c0);
-  r.kmB = ld_nt4(pg + kmeta_off(G) + 4 * (c0 + 8));
+  r.kmB = ld_nt4(pg + kmeta_off(G) + 4 * (c0 + 4));
 #pragma unroll
   for (int T = 0; T < GqaPage<G>::KT; ++T) r.kc[T] = ld_nt2(pg + (16 * T + j) * (D / 4) + 8 * g);
 #pragma unroll
   for (int k = 0; k < GqaPage<G>::PPL; ++k) {
     const int t0 = pair_token<G>(min(lane + 64 * k, NP - 1));
     r.vm[k][0] = ld_nt1(pg + vmeta_off(G) + 4 * t0);
-    r.vm[k][1] = ld_nt1(pg + vmeta_off(G) + 4 * (t0 + 8));
+    r.vm[k][1] = ld_nt1(pg + vmeta_off(G) + 4 * (t0 + 2));
   }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
@@ -190,7 +185,7 @@ __device__ __forceinline__ void gqa_load(GqaPage<G>& r, const uint8_t* __restric
 
 template <int G, int QB>
 __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
-                                         const float (&qs)[Geo<G, QB>::QPL][8], uint32_t one,
+                                         const float (&qs)[Geo<G, QB>::QPL][8],
                                          GqaLds<G, QB>& L, GqaState<QB>& st, int lane) {
   using Gm = Geo<G, QB>;
   const int j = lane & 15, g = lane >> 4;
@@ -200,12 +195,13 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
   const auto& vm = r.vm;
   const auto& vc = r.vc;
 
-  // ---- q' = qs * scale_c for the lane's 8 channels; with codes entering as
-  // 1 + c/4: z = sum qs (min_c - 4 scale_c) + 4 sum q' (1 + c/4)
+  // ---- q' = qs * scale_c for the lane's 8 channels (slot order); with codes
+  // entering as c/2: z = sum qs min_c + 2 sum q' c/2
   float scl[8], mnv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t w = (e & 1) ? dw(kmB, e >> 1) : dw(kmA, e >> 1);
+    const int c = kPerm(e);
+    const uint32_t w = c < 4 ? dw(kmA, c) : dw(kmB, c - 4);
     mnv[e] = lo_f(w);
     scl[e] = hi_f(w);
   }
@@ -217,7 +213,7 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qp[k][e] = qs[k][e] * scl[e];
-      bp[k] = fmaf(qs[k][e], fmaf(-4.0f, scl[e], mnv[e]), bp[k]);
+      bp[k] = fmaf(qs[k][e], mnv[e], bp[k]);
       amax = fmaxf(amax, fabsf(qp[k][e]));
     }
   }
@@ -225,7 +221,7 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
   const float mx = wave_max(amax);
   const int sh = max(0, __builtin_amdgcn_frexp_expf(mx) - 15);
   const float down = __builtin_amdgcn_ldexpf(1.0f, -sh);
-  const float zsc = __builtin_amdgcn_ldexpf(4.0f, sh);  // D -> log2 score units
+  const float zsc = __builtin_amdgcn_ldexpf(2.0f, sh);  // D -> log2 score units
 #pragma unroll
   for (int k = 0; k < Gm::QPL; ++k) {
     const int h = g + 4 * k;
@@ -257,8 +253,8 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
     h8 b[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      codes_b(kc[T + u].x, one, b[u][0], b[u][1]);
-      codes_b(kc[T + u].y, one, b[u][2], b[u][3]);
+      codes_b(kc[T + u].x, b[u][0], b[u][1]);
+      codes_b(kc[T + u].y, b[u][2], b[u][3]);
     }
     f4 d[2][Gm::NA];
 #pragma unroll
@@ -301,7 +297,7 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
     const int t0 = pair_token<G>(min(pi, Gm::NP - 1));
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const int t = t0 + 8 * s2;
+      const int t = t0 + 2 * s2;
       const bool ok = pv && t < n_valid;
       float zr[Gm::ZR];
 #pragma unroll
@@ -366,8 +362,6 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
 #pragma unroll
     for (int h = 0; h < QB; ++h) {
       const f16x2 two{_Float16(pp[0][h]), _Float16(pp[1][h])};
-      // the constant part of 1 + c/4, taken with the rounded p'
-      st.vmin[h] = __builtin_amdgcn_fdot2(two, f16x2{-4.0f16, -4.0f16}, st.vmin[h], false);
       if (pv) prow[4 * h] = __builtin_bit_cast(uint32_t, two);
     }
   }
@@ -382,7 +376,7 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
 #pragma unroll
     for (int w = 0; w < Gm::VDW; ++w) {
       h8 b0, b1;
-      codes_b(vc[ct][w], one, b0, b1);
+      codes_b(vc[ct][w], b0, b1);
       st.acc[ct] = mfma16(av[2 * w], b0, st.acc[ct]);
       st.acc[ct] = mfma16(av[2 * w + 1], b1, st.acc[ct]);
     }
@@ -472,7 +466,7 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const int c = 16 * ct + j;
-          const float v = (L.zs[c] + L.zs[D + c] + L.zs[2 * D + c] + L.zs[3 * D + c]) * 0.25f;
+          const float v = (L.zs[c] + L.zs[D + c] + L.zs[2 * D + c] + L.zs[3 * D + c]) * 0.5f;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (4 * g + r == h) st.acc[ct][r] = v;
@@ -481,41 +475,34 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
       }
     }
 
-    // the lane's query values for the q' step: heads g + 4k, its chunk's channels
+    // the lane's query values for the q' step: heads g + 4k, channels
+    // 8j + kPerm(slot)
     float qs[Gm::QPL][8];
-    {
-      const int cg = j >> 2, cb = j & 3;
-      const int c0 = 32 * cg + 16 * (cb >> 1) + 4 * (cb & 1);
 #pragma unroll
-      for (int k = 0; k < Gm::QPL; ++k) {
-        const int h = g + 4 * k;
-        if (h < QB) {
-          const uint2 qa = *reinterpret_cast<const uint2*>(qbase + size_t(h) * D + c0);
-          const uint2 qb = *reinterpret_cast<const uint2*>(qbase + size_t(h) * D + c0 + 8);
-          qs[k][0] = lo_f(qa.x) * qscale;  // channel c0
-          qs[k][1] = lo_f(qb.x) * qscale;  // c0 + 8
-          qs[k][2] = hi_f(qa.x) * qscale;  // c0 + 1
-          qs[k][3] = hi_f(qb.x) * qscale;  // c0 + 9
-          qs[k][4] = lo_f(qa.y) * qscale;  // c0 + 2
-          qs[k][5] = lo_f(qb.y) * qscale;  // c0 + 10
-          qs[k][6] = hi_f(qa.y) * qscale;  // c0 + 3
-          qs[k][7] = hi_f(qb.y) * qscale;  // c0 + 11
-        } else {
+    for (int k = 0; k < Gm::QPL; ++k) {
+      const int h = g + 4 * k;
+      if (h < QB) {
+        const uint4 q8 = *reinterpret_cast<const uint4*>(qbase + size_t(h) * D + 8 * j);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qs[k][e] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const int c = kPerm(e);
+          const uint32_t w = dw(q8, c >> 1);
+          qs[k][e] = ((c & 1) ? hi_f(w) : lo_f(w)) * qscale;
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[k][e] = 0.f;
       }
     }
 
     // pages, each wave every 4th
-    const uint32_t one = ones_f16x2();
     for (int u = sp.p0 + wave; u < sp.p1; u += kWaves) {
       GqaPage<G> pr;
       gqa_load<G>(pr, pages + size_t(u) * PB, lane);
-      gqa_page<G, QB>(pr, page_nvalid(a.G, a.P, u), qs, one, L, st, lane);
+      gqa_page<G, QB>(pr, page_nvalid(a.G, a.P, u), qs, L, st, lane);
     }
 
-    // this wave's state -> LDS: fin[h][c] = sum p' c + sum p min = 4 acc + vmin
+    // this wave's state -> LDS: fin[h][c] = sum p' c + sum p min = 2 acc + vmin
     float vt[QB];
 #pragma unroll
     for (int h = 0; h < QB; ++h) {
@@ -532,7 +519,7 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
       const float v = row_pick<QB>(vt, g, r);
       if (h < QB) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) L.zs[h * D + 16 * ct + j] = fmaf(st.acc[ct][r], 4.0f, v);
+        for (int ct = 0; ct < 8; ++ct) L.zs[h * D + 16 * ct + j] = fmaf(st.acc[ct][r], 2.0f, v);
       }
     }
     __syncthreads();
