@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
 }
 
 // ---------------------------------------------------------------------------
-// quantize: one work-group per (sequence, KV head) with a full window
+// quantize: one work-group (1024 threads) per (sequence, KV head) with a full
+// window
 // ---------------------------------------------------------------------------
 
 // 2-bit code of x against (min m, scale s): clamp(rint(y), 0, 3) with
@@ -78,15 +79,20 @@ __device__ __forceinline__ uint32_t qcode(float x, const CodeThr& q) {
 }
 
 constexpr int kStageRows = 128;  // member rows staged in LDS at a time (32 KiB)
+constexpr int kQuantThreads = 1024;  // 16 waves: 4 per SIMD of the CU
+constexpr int kMinMaxParts = kQuantThreads / D;  // partial K min/max per channel
 
 struct QuantLds {
   __half* stage;  // [kStageRows][D]
-  CodeThr* kq;    // [D] per channel: K min and code thresholds
+  CodeThr* kq;    // [D] per channel c at (c % 16) * 8 + c / 16: K min and code thresholds
   CodeThr* vq;    // [G] per member: V min and code thresholds
+  float* klo;     // [kMinMaxParts][D] partial K minima
+  float* khi;     // [kMinMaxParts][D] partial K maxima
   double* n2;
   int* pos;
   int* src;
   int* rank;
+  int* idx;       // member index of a candidate (counting)
   int* mem;
 };
 
@@ -95,11 +101,14 @@ __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
   q.stage = reinterpret_cast<__half*>(base);
   q.kq = reinterpret_cast<CodeThr*>(base + kStageRows * D * sizeof(__half));
   q.vq = q.kq + D;
-  q.n2 = reinterpret_cast<double*>(q.vq + G);
+  q.klo = reinterpret_cast<float*>(q.vq + G);
+  q.khi = q.klo + kMinMaxParts * D;
+  q.n2 = reinterpret_cast<double*>(q.khi + kMinMaxParts * D);
   q.pos = reinterpret_cast<int*>(q.n2 + NCmax);
   q.src = q.pos + NCmax;
   q.rank = q.src + NCmax;
-  q.mem = q.rank + NCmax;
+  q.idx = q.rank + NCmax;
+  q.mem = q.idx + NCmax;
   return q;
 }
 
@@ -114,7 +123,7 @@ __device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, R
   }
 }
 
-__global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const int h = blockIdx.x, b = blockIdx.y;
   const int bh = b * a.Hkv + h;
@@ -173,56 +182,78 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
   }
   __syncthreads();
 
-  // 2. rank under (norm, position); branch-free so the LDS reads pipeline
+  // 2. rank under (norm, position): each candidate's comparisons are split
+  //    over `parts` threads (branch-free, so the LDS reads pipeline) and the
+  //    counts summed with LDS atomics
+  const int parts = max(1, int(blockDim.x) / NC);
+  const int span = (NC + parts - 1) / parts;
   for (int i = tid; i < NC; i += blockDim.x) {
+    s.rank[i] = 0;
+    s.idx[i] = 0;
+  }
+  __syncthreads();
+  for (int x = tid; x < NC * parts; x += blockDim.x) {
+    const int i = x % NC, j0 = (x / NC) * span, j1 = min(NC, j0 + span);
     const double ni = s.n2[i];
     const int pi = s.pos[i];
     int r = 0;
-#pragma unroll 8
-    for (int j = 0; j < NC; ++j) {
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) {
       const double nj = s.n2[j];
       const int pj = s.pos[j];
       r += int(nj < ni) | (int(nj == ni) & int(pj < pi));
     }
-    s.rank[i] = r;
+    atomicAdd(&s.rank[i], r);
   }
   __syncthreads();
 
-  // 3. members (rank >= npc) in position order
-  for (int i = tid; i < NC; i += blockDim.x) {
+  // 3. members (rank >= npc) in position order, counted the same way
+  for (int x = tid; x < NC * parts; x += blockDim.x) {
+    const int i = x % NC, j0 = (x / NC) * span, j1 = min(NC, j0 + span);
     if (s.rank[i] >= npc) {
       const int pi = s.pos[i];
-      int idx = 0;
-#pragma unroll 8
-      for (int j = 0; j < NC; ++j) idx += int(s.rank[j] >= npc) & int(s.pos[j] < pi);
-      s.mem[idx] = i;
+      int c = 0;
+#pragma unroll 4
+      for (int j = j0; j < j1; ++j) c += int(s.rank[j] >= npc) & int(s.pos[j] < pi);
+      atomicAdd(&s.idx[i], c);
     }
   }
+  __syncthreads();
+  for (int i = tid; i < NC; i += blockDim.x)
+    if (s.rank[i] >= npc) s.mem[s.idx[i]] = i;
   __syncthreads();
 
   uint8_t* pg = page_ptr(a, bh, nb);
   const int n_chunks = (n_valid + kStageRows - 1) / kStageRows;
-  // 4. Key (min, scale) per channel over the members
+  // 4. Key (min, scale) per channel over the members: kMinMaxParts partial
+  //    scans per channel, then one thread per channel combines them
   {
     float lo = INFINITY, hi = -INFINITY;
+    const int c = tid % D, part = tid / D;  // blockDim.x == kMinMaxParts * D
     for (int ch = 0; ch < n_chunks; ++ch) {
       const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
       stage_rows(s, t0, cnt, krow);
       __syncthreads();
-      if (tid < D) {
-#pragma unroll 8
-        for (int t = 0; t < cnt; ++t) {
-          const float x = __half2float(s.stage[t * D + tid]);
-          lo = fminf(lo, x);
-          hi = fmaxf(hi, x);
-        }
+#pragma unroll 4
+      for (int t = part; t < cnt; t += kMinMaxParts) {
+        const float x = __half2float(s.stage[t * D + c]);
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
       }
       __syncthreads();
     }
+    s.klo[part * D + c] = lo;
+    s.khi[part * D + c] = hi;
+    __syncthreads();
     if (tid < D) {
+#pragma unroll
+      for (int p2 = 1; p2 < kMinMaxParts; ++p2) {
+        lo = fminf(lo, s.klo[p2 * D + tid]);
+        hi = fmaxf(hi, s.khi[p2 * D + tid]);
+      }
       if (n_valid == 0) lo = hi = 0.f;
       const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
-      s.kq[tid] = code_thresholds(lo, __half2float(sc));
+      s.kq[(tid % 16) * (D / 16) + tid / 16] = code_thresholds(lo, __half2float(sc));
       const uint32_t word = uint32_t(__half_as_ushort(__float2half_rn(lo))) |
                             (uint32_t(__half_as_ushort(sc)) << 16);
       reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = word;
@@ -238,9 +269,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
       __syncthreads();
     }
     const int jk = tid % (D / 16);  // this thread's 16 channels: 16*jk .. 16*jk+15
-    CodeThr kq[16];
+    CodeThr kq[16];  // the 8 blocks a wave reads for one cc are 128 contiguous bytes
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) kq[cc] = s.kq[16 * jk + cc];
+    for (int cc = 0; cc < 16; ++cc) kq[cc] = s.kq[cc * (D / 16) + jk];
     for (int w = tid; w < cnt * (D / 16); w += blockDim.x) {
       const int t = w / (D / 16), j = jk;
       const uint4* row = reinterpret_cast<const uint4*>(s.stage + t * D + 16 * j);
@@ -267,19 +298,31 @@ __global__ __launch_bounds__(256) void quantize_kernel(Arena a) {
     const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
     stage_rows(s, t0, cnt, vrow);
     __syncthreads();
-    if (tid < cnt) {
-      const __half* row = s.stage + tid * D;
+    {
+      // 8 lanes per member, 16 channels each (rotated per member against bank
+      // conflicts), combined with cross-lane swaps inside the 8
+      const int t = tid >> 3, part = tid & 7;
       float mn = INFINITY, mx = -INFINITY;
-#pragma unroll 8
-      for (int i = 0; i < D; ++i) {
-        const float x = __half2float(row[(i + 2 * tid) % D]);  // rotated: fewer bank conflicts
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
+      if (t < cnt) {
+        const __half* row = s.stage + t * D;
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+          const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
       }
-      const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
-      s.vq[t0 + tid] = code_thresholds(mn, __half2float(sc));
-      vmeta[t0 + tid] = uint32_t(__half_as_ushort(__float2half_rn(mn))) |
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+      }
+      if (t < cnt && part == 0) {
+        const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+        s.vq[t0 + t] = code_thresholds(mn, __half2float(sc));
+        vmeta[t0 + t] = uint32_t(__half_as_ushort(__float2half_rn(mn))) |
                         (uint32_t(__half_as_ushort(sc)) << 16);
+      }
     }
     __syncthreads();
     // dwords whose 16 slots start inside this chunk (chunks are multiples of 16)
@@ -347,13 +390,20 @@ hipError_t launch_append(const Arena& a, const void* k, const void* v, const App
 size_t quantize_lds_bytes(int G, int P) {
   using dev::D;
   const size_t nc = size_t(P) + G;
-  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) + nc * sizeof(double) +
-         3 * nc * sizeof(int) + G * sizeof(int);
+  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
+         2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
+         G * sizeof(int);
 }
 
 hipError_t launch_quantize(const Arena& a, hipStream_t s) {
   dim3 grid(a.Hkv, a.B);
-  hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), quantize_lds_bytes(a.G, a.P), s, a);
+  const size_t lds = quantize_lds_bytes(a.G, a.P);
+  if (lds > 65536) {  // the largest pools need more than the default dynamic LDS limit
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quantize_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(kQuantThreads), lds, s, a);
   return hipGetLastError();
 }
 
