@@ -295,6 +295,7 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   };
   int n = 0;
   for (int u = sp.p0 + wave; u < p1; u += kWaves, ++n) {
+    prio_by_work_left((p1 - u + kWaves - 1) / kWaves);
     PageRegs<G> pr;
     load_page<G>(pr, pages + size_t(u) * PB, lane);
     compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);

@@ -90,6 +90,18 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
                                 false);
 }
 
+// Issue priority from the pages a wave still has to process: the hardware
+// favours older waves among equals, so without this the work-groups sharing a
+// CU finish one after another and the CU runs its last stretch with few waves
+// (little latency hiding). Waves with more work left go first instead, so the
+// work-groups progress together. rem is wave-uniform.
+__device__ __forceinline__ void prio_by_work_left(int rem) {
+  if (rem >= 6) __builtin_amdgcn_s_setprio(3);
+  else if (rem >= 4) __builtin_amdgcn_s_setprio(2);
+  else if (rem >= 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // dword j (0..3) of a 16-byte vector
 __device__ __forceinline__ uint32_t dw(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;

@@ -497,6 +497,7 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
 
     // pages, each wave every 4th
     for (int u = sp.p0 + wave; u < sp.p1; u += kWaves) {
+      prio_by_work_left((sp.p1 - u + kWaves - 1) / kWaves);
       GqaPage<G> pr;
       gqa_load<G>(pr, pages + size_t(u) * PB, lane);
       gqa_page<G, QB>(pr, page_nvalid(a.G, a.P, u), qs, L, st, lane);
