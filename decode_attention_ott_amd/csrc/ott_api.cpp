@@ -17,6 +17,9 @@ struct ott_ctx {
   std::vector<int32_t> L, rcnt, head, nb;  // identical for every KV head of a sequence
   int32_t forced_splits = 0;
   int64_t slots = 1024;  // decode work-groups the GPU holds at once
+  int32_t cus = 256;     // compute units (work-group i and i + cus share a CU)
+  ott::HeadOrder order{};  // rebuilt at every one-split decode
+  std::vector<int32_t> seq_by_size;
   bool poisoned = false;
 };
 
@@ -165,6 +168,7 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
     int wpc = ott::decode_wgs_per_cu(a);
     if (wpc <= 0) wpc = 4;
     h->slots = int64_t(cus) * wpc;
+    h->cus = cus;
   }
   if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess ||
       hipMemset(a.base + lay.off_split_sync, 0, sync_bytes) != hipSuccess) {
@@ -252,7 +256,36 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, bytes_max / (3 * int64_t(h->lay.page_bytes)))));
   }
   S = std::max(1, std::min(S, h->dev.max_splits));
-  return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, static_cast<hipStream_t>(stream)));
+  // One split per head and heads of unequal size: deal the heads to CUs
+  // largest first, in snake order over the rounds of `cus` work-groups, so
+  // that each CU's total is about the same.
+  ott::HeadOrder& ord = h->order;
+  ord.n = 0;
+  const int Hkv = h->cfg.num_kv_heads;
+  const int64_t heads = int64_t(B) * Hkv;
+  if (S == 1 && heads <= ott::kMaxOrdered && heads > h->cus) {
+    std::vector<int32_t>& seq = h->seq_by_size;
+    seq.resize(B);
+    for (int b = 0; b < B; ++b) seq[b] = b;
+    auto bytes = [&](int b) {
+      const int64_t pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
+      return int64_t(h->nb[b]) * int64_t(h->lay.page_bytes) + (pc + h->rcnt[b]) * 4 * h->cfg.head_dim;
+    };
+    std::stable_sort(seq.begin(), seq.end(), [&](int x, int y) { return bytes(x) > bytes(y); });
+    const int64_t C = h->cus;
+    int64_t p = 0;
+    for (int b : seq) {
+      for (int hh = 0; hh < Hkv; ++hh, ++p) {
+        const int64_t r = p / C, i = p % C;
+        const int64_t slot = r * C + ((r & 1) ? C - 1 - i : i);
+        ord.bh[slot] = uint16_t(b * Hkv + hh);
+      }
+    }
+    // a partial last round leaves holes: fall back to the identity
+    ord.n = (heads % C == 0) ? int32_t(heads) : 0;
+  }
+  return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, ord,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 void ott_destroy(ott_handle_t h) { delete h; }

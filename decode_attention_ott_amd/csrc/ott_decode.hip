@@ -234,14 +234,15 @@ struct alignas(16) WaveLds {
 // G <= 128 fits 128 VGPRs (4 waves per SIMD); G = 256 keeps two waves per SIMD.
 template <int G>
 __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, const __half* __restrict__ q,
-                                                     __half* __restrict__ out, int S) {
+                                                     __half* __restrict__ out, int S,
+                                                     HeadOrder order) {
   __shared__ WaveLds lds_all[kWaves];
   __shared__ float mg_m[kWaves], mg_l[kWaves];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   WaveLds& L = lds_all[wave];
   const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;  // = b * H + h, also the query head's index
+  const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);  // = b * H + h
   const int b = bh / a.Hkv;
 
   const int32_t* ctr = counters(a, bh);
@@ -376,18 +377,19 @@ int decode_wgs_per_cu(const Arena& a) {
   return e == hipSuccess ? n : 0;
 }
 
-hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, hipStream_t s) {
+hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, const HeadOrder& order,
+                         hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);
   hipError_t e;
   if (a.Hq != a.Hkv) {
-    e = launch_decode_gqa(a, q, out, S, s);
+    e = launch_decode_gqa(a, q, out, S, order, s);
   } else {
     const dim3 grid(unsigned(a.B) * a.Hkv * S);
     switch (a.G) {
-      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
-      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
-      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S); break;
+      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
+      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
+      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();

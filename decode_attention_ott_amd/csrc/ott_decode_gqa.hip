@@ -390,7 +390,8 @@ __device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
 // LDS. More than QB heads per KV head run as several passes.
 template <int G, int QB>
 __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ? 3 : 2) void decode_gqa_kernel(Arena a, const __half* __restrict__ q,
-                                                         __half* __restrict__ out, int S) {
+                                                         __half* __restrict__ out, int S,
+                                                         HeadOrder order) {
   using Gm = Geo<G, QB>;
   __shared__ GqaLds<G, QB> lds_all[kWaves];
   __shared__ float mg_m[kWaves][QB], mg_l[kWaves][QB];
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
   GqaLds<G, QB>& L = lds_all[wave];
   const int NQ = a.Hq / a.Hkv;
   const int s = blockIdx.x % S;
-  const int bh = blockIdx.x / S;
+  const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
 
   const int32_t* ctr = counters(a, bh);
@@ -553,17 +554,18 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
 }
 
 template <int G>
-hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, hipStream_t s) {
+hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, const HeadOrder& order,
+                    hipStream_t s) {
   const int NQ = a.Hq / a.Hkv;
   const dim3 grid(unsigned(a.B) * a.Hkv * S), block(64 * kWaves);
   if (NQ % 16 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 16>), grid, block, 0, s, a, q, out, S);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 16>), grid, block, 0, s, a, q, out, S, order);
   } else if (NQ % 8 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 8>), grid, block, 0, s, a, q, out, S);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 8>), grid, block, 0, s, a, q, out, S, order);
   } else if (NQ % 4 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 4>), grid, block, 0, s, a, q, out, S);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 4>), grid, block, 0, s, a, q, out, S, order);
   } else if (NQ == 2) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S, order);
   } else {
     return hipErrorInvalidValue;
   }
@@ -594,13 +596,14 @@ int decode_gqa_wgs_per_cu(const Arena& a) {
   }
 }
 
-hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int S, hipStream_t s) {
+hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int S,
+                             const HeadOrder& order, hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);
   switch (a.G) {
-    case 64: return launch_g<64>(a, qh, oh, S, s);
-    case 128: return launch_g<128>(a, qh, oh, S, s);
-    case 256: return launch_g<256>(a, qh, oh, S, s);
+    case 64: return launch_g<64>(a, qh, oh, S, order, s);
+    case 128: return launch_g<128>(a, qh, oh, S, order, s);
+    case 256: return launch_g<256>(a, qh, oh, S, order, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,14 +30,24 @@ struct AppendCounts {
   uint16_t n[kMaxBatch];
 };
 
+// Which (sequence, KV head) work-group i of a one-split decode serves. The
+// dispatcher places work-groups i, i + CUs, i + 2 CUs, ... on one CU, so the
+// host orders heads by size to even out each CU's total (n = 0: identity).
+constexpr int kMaxOrdered = 1024;
+struct HeadOrder {
+  int32_t n;
+  uint16_t bh[kMaxOrdered];
+};
+
 hipError_t launch_append(const Arena& a, const void* k, const void* v, const AppendCounts& n,
                          hipStream_t s);
 hipError_t launch_quantize(const Arena& a, hipStream_t s);
-hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits, hipStream_t s);
+hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
+                         const HeadOrder& order, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it
 // writes the output (one split) or the split partials like launch_decode.
 hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int num_splits,
-                             hipStream_t s);
+                             const HeadOrder& order, hipStream_t s);
 // Work-groups of the decode kernel this arena's shape launches that fit on
 // one CU at once (0 if the runtime cannot tell).
 int decode_wgs_per_cu(const Arena& a);
