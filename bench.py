@@ -45,6 +45,15 @@ def algorithmic_decode_bytes(layer) -> int:
     return total + 512 * layer.B * layer.Hq
 
 
+def auto_states(w, lengths) -> int:
+    """States per lap so that one lap reads >= 3 x 256 MB (3..8)."""
+    page = w.group_size * w.head_dim // 2 + 4 * w.head_dim + 4 * w.group_size
+    per_head = [(int(L) // w.group_size) * page + (w.pool_size + w.residual + w.group_size // 2) * 4 * w.head_dim
+                for L in lengths]
+    state = w.num_kv_heads * sum(per_head)
+    return int(min(8, max(3, -(-3 * 256e6 // max(state, 1)))))
+
+
 def decode_kernel_name(w) -> str:
     """The decode kernel a workload launches (the split combine kernel follows
     it when a launch uses more than one split)."""
@@ -130,7 +139,9 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="llama2-7b-b32")
-    ap.add_argument("--states", type=int, default=3)
+    ap.add_argument("--states", type=int, default=0,
+                    help="independent layer states stepped round-robin (0: enough that one lap "
+                         "over them reads >= 3 x 256 MB, the Infinity Cache size; 3..8)")
     ap.add_argument("--splits", type=int, default=0, help="split-K factor (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -149,6 +160,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     lengths = synth.prefill_lengths(w)
+    if args.states <= 0:
+        args.states = auto_states(w, lengths)
     n_steps_state = (args.warmup + args.steps + args.states - 1) // args.states + 1
     n_pos = int(lengths.max()) + n_steps_state
     print(f"[bench] generating {w.name} inputs ({n_pos} positions)", file=sys.stderr, flush=True)
@@ -212,22 +225,27 @@ def main():
     ms_per_step = total_ms / args.steps
     tokens_per_s = w.batch * args.steps / (total_ms / 1e3)
     # The decode alone, launched back to back over the states (state is not
-    # modified by a decode): per-launch duration, the figure the roofline uses.
-    n_dec = 8 * args.states
+    # modified by a decode): 5 laps of >= 20 launches each, the median lap's
+    # per-launch duration is the figure the roofline uses.
+    per_lap = args.states * -(-20 // args.states)
     dec_bytes = [algorithmic_decode_bytes(lay) for lay in layers]
     q_last = qd[args.warmup + args.steps - 1]
     for i in range(args.states):
         L.ott_decode(layers[i].handle, q_last.data_ptr(), outd.data_ptr(), sp)
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record(stream)
-    for i in range(n_dec):
-        L.ott_decode(layers[i % args.states].handle, q_last.data_ptr(), outd.data_ptr(), sp)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_only_us = 1e3 * d0.elapsed_time(d1) / n_dec
-    bytes_per_launch = sum(dec_bytes[i % args.states] for i in range(n_dec)) / n_dec
+    laps = []
+    for lap in range(5):
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for i in range(per_lap):
+            L.ott_decode(layers[i % args.states].handle, q_last.data_ptr(), outd.data_ptr(), sp)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        laps.append(1e3 * d0.elapsed_time(d1) / per_lap)
+    dec_only_us = sorted(laps)[len(laps) // 2]
+    n_dec = 5 * per_lap
+    bytes_per_launch = sum(dec_bytes) / len(dec_bytes)
     achieved = bytes_per_launch / (dec_only_us * 1e-6) / 1e9
     traffic = load_traffic(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -235,6 +253,7 @@ def main():
                 "traffic": traffic,
                 "kernel": decode_kernel_name(w),
                 "decode_us": round(dec_only_us, 2),
+                "decode_launches": n_dec,
                 "alg_bytes_per_launch": int(bytes_per_launch)}
     cpu = None
     if not args.no_cpu_baseline:
