@@ -203,7 +203,10 @@ ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const 
   ott::AppendCounts cnt{};
   cnt.max_new = max_new;
   cnt.uniform = uniform ? h_n_new[0] : -1;
-  for (int b = 0; b < B; ++b) cnt.n[b] = uint16_t(h_n_new[b]);
+  for (int b = 0; b < B; ++b) {
+    cnt.n[b] = uint16_t(h_n_new[b]);
+    cnt.slot0[b] = uint16_t((h->head[b] + h->rcnt[b]) % C);
+  }
   st = after_launch(h, ott::launch_append(h->dev, d_k, d_v, cnt, static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
   for (int b = 0; b < B; ++b) {

@@ -23,11 +23,14 @@ struct Arena {
   float sm_scale;
 };
 
-// New-token counts of one ott_append call (uint16 keeps the kernel argument at 1 KiB).
+// New-token counts of one ott_append call and the window slot of each
+// sequence's first new token (known to the host, so the kernel's copies do
+// not wait for a counter read); uint16 keeps the kernel argument at 2 KiB.
 struct AppendCounts {
   int32_t max_new;
   int32_t uniform;  // >= 0: every sequence appends this many; < 0: use n[]
   uint16_t n[kMaxBatch];
+  uint16_t slot0[kMaxBatch];
 };
 
 // Which (sequence, KV head) work-group i of a one-split decode serves. The

@@ -29,21 +29,21 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
   const int bh = b * a.Hkv + h;
   const int n = cnt.uniform >= 0 ? cnt.uniform : int(cnt.n[b]);
   if (n == 0) return;
-  int32_t* ctr = counters(a, bh);
-  const int r_cnt = ctr[1], head = ctr[2];
   uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
   uint4* rv = reinterpret_cast<uint4*>(ring_v(a, bh));
   const size_t src = size_t(bh) * cnt.max_new * (D / 8);
+  const int slot0 = cnt.slot0[b];
   for (int i = threadIdx.x; i < n * (D / 8); i += blockDim.x) {
     const int t = i / (D / 8), c = i % (D / 8);
-    const int slot = (head + r_cnt + t) % a.C;
+    int slot = slot0 + t;
+    slot -= (slot / a.C) * a.C;
     rk[size_t(slot) * (D / 8) + c] = k[src + i];
     rv[size_t(slot) * (D / 8) + c] = v[src + i];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {  // the only thread touching this head's counters here
+    int32_t* ctr = counters(a, bh);
     ctr[0] += n;
-    ctr[1] = r_cnt + n;
+    ctr[1] += n;
   }
 }
 
