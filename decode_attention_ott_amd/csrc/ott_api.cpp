@@ -19,6 +19,7 @@ struct ott_ctx {
   int64_t slots = 1024;  // decode work-groups the GPU holds at once
   int32_t cus = 256;     // compute units (work-group i and i + cus share a CU)
   ott::HeadOrder order{};  // rebuilt at every one-split decode
+  ott::QuantizeList due{};  // rebuilt at every quantize call
   std::vector<int32_t> seq_by_size;
   bool poisoned = false;
 };
@@ -220,11 +221,14 @@ ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_qua
   ott_status_t st = check_handle(h);
   if (st != OTT_OK) return st;
   const int B = h->cfg.batch, C = h->dev.C, G = h->dev.G;
-  int ready = 0;
-  for (int b = 0; b < B; ++b) ready += (h->rcnt[b] >= C);
+  ott::QuantizeList& due = h->due;
+  due.n = 0;
+  for (int b = 0; b < B; ++b)
+    if (h->rcnt[b] >= C) due.b[due.n++] = uint16_t(b);
+  const int ready = due.n;
   if (n_seq_quantized) *n_seq_quantized = 0;
   if (ready == 0) return OTT_OK;
-  st = after_launch(h, ott::launch_quantize(h->dev, static_cast<hipStream_t>(stream)));
+  st = after_launch(h, ott::launch_quantize(h->dev, due, static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
   for (int b = 0; b < B; ++b) {
     if (h->rcnt[b] >= C) {

@@ -44,7 +44,12 @@ struct HeadOrder {
 
 hipError_t launch_append(const Arena& a, const void* k, const void* v, const AppendCounts& n,
                          hipStream_t s);
-hipError_t launch_quantize(const Arena& a, hipStream_t s);
+// The sequences whose window is full at an ott_quantize_group call.
+struct QuantizeList {
+  int32_t n;
+  uint16_t b[kMaxBatch];
+};
+hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
                          const HeadOrder& order, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it

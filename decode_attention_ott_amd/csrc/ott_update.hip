@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
 
 // ---------------------------------------------------------------------------
 // quantize: one work-group (1024 threads) per (sequence, KV head) with a full
-// window
+// window; the host launches only the sequences that are due
 // ---------------------------------------------------------------------------
 
 // 2-bit code of x against (min m, scale s): clamp(rint(y), 0, 3) with
@@ -123,9 +123,9 @@ __device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, R
   }
 }
 
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a) {
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, QuantizeList due) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x, b = due.b[blockIdx.y];
   const int bh = b * a.Hkv + h;
   const int G = a.G, P = a.P, C = a.C;
   int32_t* ctr = counters(a, bh);
@@ -395,15 +395,15 @@ size_t quantize_lds_bytes(int G, int P) {
          G * sizeof(int);
 }
 
-hipError_t launch_quantize(const Arena& a, hipStream_t s) {
-  dim3 grid(a.Hkv, a.B);
+hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s) {
+  dim3 grid(a.Hkv, due.n);
   const size_t lds = quantize_lds_bytes(a.G, a.P);
   if (lds > 65536) {  // the largest pools need more than the default dynamic LDS limit
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quantize_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(quantize_kernel, grid, dim3(kQuantThreads), lds, s, a);
+  hipLaunchKernelGGL(quantize_kernel, grid, dim3(kQuantThreads), lds, s, a, due);
   return hipGetLastError();
 }
 
