@@ -344,20 +344,40 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   }
 }
 
-// Merge of S split partial states per (sequence, query head).
+// Merge of S split partial states per (sequence, query head): the partials
+// are read 16 at a time with all loads in flight, then merged online
+// (M, L, A) <- (max, L e^(M-M') + sum l e^(m-M'), A e^(M-M') + sum acc e^(m-M')).
 __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict__ out, int S) {
+  constexpr int kChunk = 16;
   const int bq = blockIdx.x;  // b * Hq + qh
   const int c = threadIdx.x;
   const float* part = reinterpret_cast<const float*>(a.base + a.off_partials) +
                       size_t(bq) * a.max_splits * (2 + D);
-  float M = -INFINITY;
-  for (int i = 0; i < S; ++i) M = fmaxf(M, part[i * (2 + D)]);
-  float Ls = 0.f, A = 0.f;
-  for (int i = 0; i < S; ++i) {
-    const float m = part[i * (2 + D)];
-    const float f = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    Ls = fmaf(part[i * (2 + D) + 1], f, Ls);
-    A = fmaf(part[i * (2 + D) + 2 + c], f, A);
+  float M = -INFINITY, Ls = 0.f, A = 0.f;
+  for (int i0 = 0; i0 < S; i0 += kChunk) {
+    float m[kChunk], l[kChunk], v[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const bool ok = i0 + k < S;
+      const float* p = part + size_t(ok ? i0 + k : 0) * (2 + D);
+      m[k] = ok ? p[0] : -INFINITY;
+      l[k] = p[1];
+      v[k] = p[2 + c];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
+    if (Mc == -INFINITY) continue;
+    const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mc);
+    Ls *= f0;
+    A *= f0;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float f = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mc);
+      Ls = fmaf(l[k], f, Ls);
+      A = fmaf(v[k], f, A);
+    }
+    M = Mc;
   }
   out[size_t(bq) * D + c] = __float2half_rn(A / Ls);
 }
