@@ -92,7 +92,10 @@ struct WaveState {
   float m;        // running max (wave-uniform)
   float l;        // this lane's share of the running sum of weights
   float vmin;     // this lane's share of sum p_t * min_t over quantized tokens
-  float acc[8];   // channel 16k + lane/4, slot quarter lane&3; half units
+  // G = 128 (matrix-core pages): acc[0..3] digit-row sums of channel
+  // 16(lane>>4) + (lane&15), acc[4..7] of that channel + 64, full units.
+  // Other G: channel 16k + lane/4, slot quarter lane&3, half units.
+  float acc[8];
 };
 __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
   if (m_new == st.m) return;
@@ -220,6 +223,199 @@ __device__ __forceinline__ void compute_page(const PageRegs<G>& r, int n_valid, 
 }
 
 // ---------------------------------------------------------------------------
+// quantized pages on the matrix cores (G = 128)
+// ---------------------------------------------------------------------------
+// Both page products run on v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8
+// (E4M3) weight digits and B = the page's 2-bit codes read as FP4 (E2M1): with
+// its two high bits cleared, a code nibble is the FP4 value code/2, so a code
+// dword becomes two B dwords with two masks and no conversion.
+//
+// Operand layout of that instruction (lane l, j = l & 15, g = l >> 4):
+//   B: column j; byte-nibble n of dword w is logical k = 32g + 8w + n.
+//   A: row j; byte b is logical k = 16g + (b & 15) + 64 (b >> 4).
+//   D: column j, rows 4g..4g+3 in the four result registers.
+//   The E8M0 scale of A row r for k-block kb is the op_sel byte of lane r+16kb.
+// The lane's B chunk is 8 code bytes (32 items, item 4i+h at bits 2h of byte
+// i); after the masks, logical k holds item mx_item(k) of the page row.
+//
+// Exactness: the matrix core sums one instruction's products with a limited
+// number of bits below the largest, so every weight is split into 4
+// fixed-point digits in [-16, 16] relative to one power of two 2^e per page
+// and kind (digit k has step 2^(e-4-5k)). A row of digits times code/2 gives
+// products on one grid of half-steps, at most 24 steps each, whose sums are
+// exact; the step enters as the row's E8M0 scale. 4 digits keep 19 bits of the
+// largest weight of the page.
+//
+// Rows: A holds the 4 digit rows of the page four times (rows 4i..4i+3). The
+// scale register packs one byte per replica; byte i is the real scale for
+// replica i and 0 (2^-127) for the others, and tile T runs with op_sel T % 4.
+// Tiles 0..3 accumulate into one result and 4..7 into another, so lane group g
+// ends with exactly its own tiles g and g+4 (the masked products add at most
+// 2^-110 in total).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr uint32_t kCodeMask = 0x33333333u;
+
+// item of logical k (channel for K, slot for V), and its inverse
+__device__ __forceinline__ int mx_item(int k) {
+  return (k & ~31) | (k & 16) | ((k >> 3) & 1) | ((k & 7) << 1);
+}
+__device__ __forceinline__ int mx_k(int t) {
+  return (t & ~31) | (t & 16) | ((t & 1) << 3) | ((t & 15) >> 1);
+}
+
+__device__ __forceinline__ i32x8 mx_b(uint2 c) {
+  i32x8 b;
+  b[0] = int(c.x & kCodeMask);
+  b[1] = int((c.x >> 2) & kCodeMask);
+  b[2] = int(c.y & kCodeMask);
+  b[3] = int((c.y >> 2) & kCodeMask);
+  b[4] = 0;
+  b[5] = 0;
+  b[6] = 0;
+  b[7] = 0;
+  return b;
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x4v mx_mfma(const i32x8& a, const i32x8& b, const f32x4v& c, int sc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /* A: fp8 e4m3 */,
+                                                          4 /* B: fp4 e2m1 */, SEL, sc, 0, 127);
+}
+
+// x = sum_k d[k] 2^(e-4-5k) + r with |r| <= 2^(e-20), given |x| < 2^e
+__device__ __forceinline__ void mx_digits(float x, int e, float (&d)[4]) {
+  float r = __builtin_amdgcn_ldexpf(x, 4 - e);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    d[k] = __builtin_rintf(r);
+    r = (r - d[k]) * 32.0f;
+  }
+}
+
+// A operand: digit row (lane & 3) of a [4][128] byte block in logical k order
+__device__ __forceinline__ i32x8 mx_a(const uint8_t* rows, int lane) {
+  const uint8_t* r = rows + 128 * (lane & 3) + 16 * (lane >> 4);
+  const uint4 lo = *reinterpret_cast<const uint4*>(r);
+  const uint4 hi = *reinterpret_cast<const uint4*>(r + 64);
+  i32x8 a;
+  a[0] = int(lo.x); a[1] = int(lo.y); a[2] = int(lo.z); a[3] = int(lo.w);
+  a[4] = int(hi.x); a[5] = int(hi.y); a[6] = int(hi.z); a[7] = int(hi.w);
+  return a;
+}
+
+// Scale register: 2^(e-4-5k) for digit row k times 2 for the code/2 view, in
+// the byte of the lane's replica.
+__device__ __forceinline__ int mx_scale(int e, int lane) {
+  return (124 - 5 * (lane & 3) + e) << (8 * ((lane >> 2) & 3));
+}
+
+__device__ __forceinline__ int mx_exp(float amax) {
+  return max(__builtin_amdgcn_frexp_expf(amax), -100);
+}
+
+struct MxPage {
+  uint2 kc[8];     // K tile T: token 16T + j, channel items 32g..32g+31
+  uint2 vc[8];     // V tile C: channel 16C + j, slot items 32g..32g+31
+  uint32_t km[2];  // K (min, scale) of the lane's channels c0 and c0 + 2
+  uint32_t vm[2];  // V (min, scale) of the lane's slots 16g + j and 64 + 16g + j
+};
+
+__device__ __forceinline__ void mx_load(MxPage& r, const uint8_t* __restrict__ pg, int lane,
+                                        int c0) {
+  constexpr int G = 128;
+  const int j = lane & 15, g = lane >> 4;
+  r.km[0] = ld_nt1(pg + kmeta_off(G) + 4 * c0);
+  r.km[1] = ld_nt1(pg + kmeta_off(G) + 4 * (c0 + 2));
+#pragma unroll
+  for (int T = 0; T < 8; ++T) r.kc[T] = ld_nt2(pg + (16 * T + j) * (D / 4) + 8 * g);
+  r.vm[0] = ld_nt1(pg + vmeta_off(G) + 4 * (16 * g + j));
+  r.vm[1] = ld_nt1(pg + vmeta_off(G) + 4 * (64 + 16 * g + j));
+#pragma unroll
+  for (int C = 0; C < 8; ++C) r.vc[C] = ld_nt2(pg + vcode_off(G) + (16 * C + j) * (G / 4) + 8 * g);
+}
+
+// One page. State layout: acc[0..3] are the digit-row partial sums of channel
+// 16g + j, acc[4..7] those of channel 64 + 16g + j (full units); the lane's
+// tokens are slots 16g + j and 64 + 16g + j.
+__device__ __forceinline__ void mx_page(const MxPage& r, int n_valid, float qs0, float qs1,
+                                        uint8_t* qa, uint8_t* pa, WaveState& st, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  // ---- scores: q'_c = q_c scale_c as digits, bias = sum_c q_c min_c
+  const float qp0 = qs0 * hi_f(r.km[0]), qp1 = qs1 * hi_f(r.km[1]);
+  const float bias = wave_sum(fmaf(qs0, lo_f(r.km[0]), qs1 * lo_f(r.km[1])));
+  const int eq = mx_exp(wave_max(fmaxf(fabsf(qp0), fabsf(qp1))));
+  {
+    float d0[4], d1[4];
+    mx_digits(qp0, eq, d0);
+    mx_digits(qp1, eq, d1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<uint16_t*>(qa + 128 * k + 2 * lane) =
+          uint16_t(__builtin_amdgcn_cvt_pk_fp8_f32(d0[k], d1[k], 0, false));
+  }
+  wave_lds_sync();
+  const i32x8 aq = mx_a(qa, lane);
+  const int sq = mx_scale(eq, lane);
+  f32x4v za = {0.f, 0.f, 0.f, 0.f}, zb = za;
+  za = mx_mfma<0>(aq, mx_b(r.kc[0]), za, sq);
+  zb = mx_mfma<0>(aq, mx_b(r.kc[4]), zb, sq);
+  za = mx_mfma<1>(aq, mx_b(r.kc[1]), za, sq);
+  zb = mx_mfma<1>(aq, mx_b(r.kc[5]), zb, sq);
+  za = mx_mfma<2>(aq, mx_b(r.kc[2]), za, sq);
+  zb = mx_mfma<2>(aq, mx_b(r.kc[6]), zb, sq);
+  za = mx_mfma<3>(aq, mx_b(r.kc[3]), za, sq);
+  zb = mx_mfma<3>(aq, mx_b(r.kc[7]), zb, sq);
+  const int t0 = 16 * g + j;
+  float z0 = bias + ((za[0] + za[1]) + (za[2] + za[3]));
+  float z1 = bias + ((zb[0] + zb[1]) + (zb[2] + zb[3]));
+  if (n_valid < 128) {  // only a page built while the pool was filling is short
+    if (t0 >= n_valid) z0 = -INFINITY;
+    if (t0 + 64 >= n_valid) z1 = -INFINITY;
+  }
+  const float mx = wave_max(fmaxf(z0, z1));
+  if (mx == -INFINITY) return;  // a page without members
+  rescale_q(st, fmaxf(st.m, mx));
+  const float p0 = exp2_fast(z0 - st.m), p1 = exp2_fast(z1 - st.m);
+  st.l += p0 + p1;
+  st.vmin = fmaf(p0, lo_f(r.vm[0]), fmaf(p1, lo_f(r.vm[1]), st.vmin));
+  // ---- values: p'_t = p_t scale_t as digits
+  const float pp0 = p0 * hi_f(r.vm[0]), pp1 = p1 * hi_f(r.vm[1]);
+  const int ep = mx_exp(wave_max(fmaxf(pp0, pp1)));
+  {
+    float d0[4], d1[4];
+    mx_digits(pp0, ep, d0);
+    mx_digits(pp1, ep, d1);
+    const int kt = mx_k(t0);  // slot t0 + 64 sits at kt + 64
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(d0[k], d1[k], 0, false));
+      pa[128 * k + kt] = uint8_t(w);
+      pa[128 * k + kt + 64] = uint8_t(w >> 8);
+    }
+  }
+  wave_lds_sync();
+  const i32x8 ap = mx_a(pa, lane);
+  const int sp = mx_scale(ep, lane);
+  f32x4v va = {st.acc[0], st.acc[1], st.acc[2], st.acc[3]};
+  f32x4v vb = {st.acc[4], st.acc[5], st.acc[6], st.acc[7]};
+  va = mx_mfma<0>(ap, mx_b(r.vc[0]), va, sp);
+  vb = mx_mfma<0>(ap, mx_b(r.vc[4]), vb, sp);
+  va = mx_mfma<1>(ap, mx_b(r.vc[1]), va, sp);
+  vb = mx_mfma<1>(ap, mx_b(r.vc[5]), vb, sp);
+  va = mx_mfma<2>(ap, mx_b(r.vc[2]), va, sp);
+  vb = mx_mfma<2>(ap, mx_b(r.vc[6]), vb, sp);
+  va = mx_mfma<3>(ap, mx_b(r.vc[3]), va, sp);
+  vb = mx_mfma<3>(ap, mx_b(r.vc[7]), vb, sp);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    st.acc[k] = va[k];
+    st.acc[4 + k] = vb[k];
+  }
+  wave_lds_sync();
+}
+
+// ---------------------------------------------------------------------------
 // the kernel (one query head per KV head)
 // ---------------------------------------------------------------------------
 // Work-group = 4 waves on one (sequence, head, split). The waves deal the
@@ -257,10 +453,14 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
 
+  constexpr bool kMx = (G == 128);  // pages on the matrix cores
   const __half* qrow = q + size_t(bh) * D;
-  const uint32_t q2 = reinterpret_cast<const uint32_t*>(qrow)[lane];
   const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
-  const float qs0 = lo_f(q2) * qscale, qs1 = hi_f(q2) * qscale;
+  // the lane's two channels: 2 lane, 2 lane + 1, or for the matrix-core pages
+  // the channels of logical k = 2 lane, 2 lane + 1 (c0 and c0 + 2)
+  const int c0 = kMx ? mx_item(2 * lane) : 2 * lane;
+  const int c1 = kMx ? c0 + 2 : c0 + 1;
+  const float qs0 = __half2float(qrow[c0]) * qscale, qs1 = __half2float(qrow[c1]) * qscale;
   WaveState st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -285,21 +485,34 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
     rescale_q(st, M);
     const float af = (fs.m == -INFINITY) ? 0.f : exp2_fast(fs.m - M);
     st.l = fmaf(fs.l, af, st.l);
-    const float ah = 0.5f * af;
+    const float ah = kMx ? af : 0.5f * af;
     float4* f = reinterpret_cast<float4*>(&L.fin[lane >> 4][8 * (lane & 15)]);
     f[0] = make_float4(fs.acc[0] * ah, fs.acc[1] * ah, fs.acc[2] * ah, fs.acc[3] * ah);
     f[1] = make_float4(fs.acc[4] * ah, fs.acc[5] * ah, fs.acc[6] * ah, fs.acc[7] * ah);
     wave_lds_sync();
+    if constexpr (kMx) {
+      const int ca = 16 * (lane >> 4) + (lane & 15);
+      st.acc[0] += (L.fin[0][ca] + L.fin[1][ca]) + (L.fin[2][ca] + L.fin[3][ca]);
+      st.acc[4] += (L.fin[0][ca + 64] + L.fin[1][ca + 64]) + (L.fin[2][ca + 64] + L.fin[3][ca + 64]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
+      for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
+    }
     wave_lds_sync();
   };
   int n = 0;
   for (int u = sp.p0 + wave; u < p1; u += kWaves, ++n) {
     prio_by_work_left((p1 - u + kWaves - 1) / kWaves);
-    PageRegs<G> pr;
-    load_page<G>(pr, pages + size_t(u) * PB, lane);
-    compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
+    if constexpr (kMx) {
+      MxPage pr;
+      mx_load(pr, pages + size_t(u) * PB, lane, c0);
+      mx_page(pr, page_nvalid(a.G, a.P, u), qs0, qs1, reinterpret_cast<uint8_t*>(L.qp),
+              reinterpret_cast<uint8_t*>(L.ph), st, lane);
+    } else {
+      PageRegs<G> pr;
+      load_page<G>(pr, pages + size_t(u) * PB, lane);
+      compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
+    }
     if ((n & 3) == wave && chunk < t1) next_chunk();
   }
   while (chunk < t1) next_chunk();
@@ -307,11 +520,17 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   // this wave's state -> LDS in channel order (accumulator back to full units)
   const float l_tot = wave_sum(st.l);
   const float v_tot = wave_sum(st.vmin);
+  if constexpr (kMx) {
+    const int ca = 16 * (lane >> 4) + (lane & 15);
+    L.fin[0][ca] = ((st.acc[0] + st.acc[1]) + (st.acc[2] + st.acc[3])) + v_tot;
+    L.fin[0][ca + 64] = ((st.acc[4] + st.acc[5]) + (st.acc[6] + st.acc[7])) + v_tot;
+  } else {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) st.acc[k] = quad_sum(st.acc[k]);
-  if ((lane & 3) == 0) {
+    for (int k = 0; k < 8; ++k) st.acc[k] = quad_sum(st.acc[k]);
+    if ((lane & 3) == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) L.fin[0][16 * k + (lane >> 2)] = fmaf(2.0f, st.acc[k], v_tot);
+      for (int k = 0; k < 8; ++k) L.fin[0][16 * k + (lane >> 2)] = fmaf(2.0f, st.acc[k], v_tot);
+    }
   }
   if (lane == 0) {
     mg_m[wave] = st.m;
