@@ -26,75 +26,14 @@ namespace {
 using namespace dev;
 using namespace dec;
 
-// Dot of 16 2-bit codes (one dword, code i in bits 2i..2i+1) with 16 weights.
-// A nibble whose two high bits are zero is the FP4 (E2M1) value code/2, so two
-// masks turn the dword into 8 + 8 FP4 values and each byte converts to two
-// floats in one instruction, so the result is half the true dot product.
-__device__ __forceinline__ float dot16_codes(uint32_t w, const float4& c0, const float4& c1,
-                                             const float4& c2, const float4& c3, float acc) {
-  const uint32_t ev = w & 0x33333333u;         // codes 0 and 2 of every byte
-  const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1 and 3 of every byte
-  f32x2 e, o;
-  e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 0);
-  o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 0);
-  acc = fmaf(c0.x, e.x, acc);
-  acc = fmaf(c0.y, o.x, acc);
-  acc = fmaf(c0.z, e.y, acc);
-  acc = fmaf(c0.w, o.y, acc);
-  e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 1);
-  o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 1);
-  acc = fmaf(c1.x, e.x, acc);
-  acc = fmaf(c1.y, o.x, acc);
-  acc = fmaf(c1.z, e.y, acc);
-  acc = fmaf(c1.w, o.y, acc);
-  e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 2);
-  o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 2);
-  acc = fmaf(c2.x, e.x, acc);
-  acc = fmaf(c2.y, o.x, acc);
-  acc = fmaf(c2.z, e.y, acc);
-  acc = fmaf(c2.w, o.y, acc);
-  e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 3);
-  o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 3);
-  acc = fmaf(c3.x, e.x, acc);
-  acc = fmaf(c3.y, o.x, acc);
-  acc = fmaf(c3.z, e.y, acc);
-  acc = fmaf(c3.w, o.y, acc);
-  return acc;
-}
-
-// Same for 16 codes against fp16 weights held as pairs per group of 4 slots:
-// group g gives {(w[4g], w[4g+2]), (w[4g+1], w[4g+3])}, the order in which the
-// FP4 -> f16 conversion returns codes (0,2) and (1,3) of a byte; pa holds
-// groups 0 and 1 of the dword, pb groups 2 and 3. Half the true dot product.
-__device__ __forceinline__ float dot16_codes_h(uint32_t w, const uint4& pa, const uint4& pb,
-                                               float acc) {
-  const uint32_t ev = w & 0x33333333u;
-  const uint32_t od = (w >> 2) & 0x33333333u;
-  acc = fdot2(pa.x, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0)), acc);
-  acc = fdot2(pa.y, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0)), acc);
-  acc = fdot2(pa.z, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1)), acc);
-  acc = fdot2(pa.w, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1)), acc);
-  acc = fdot2(pb.x, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2)), acc);
-  acc = fdot2(pb.y, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2)), acc);
-  acc = fdot2(pb.z, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3)), acc);
-  acc = fdot2(pb.w, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3)), acc);
-  return acc;
-}
-
-// Position of slot s in the pair layout read by dot16_codes_h.
-__device__ __forceinline__ int pair_slot(int s) {
-  return (s & ~3) | ((s & 1) << 1) | ((s >> 1) & 1);
-}
-
 // Online softmax state of one wave (scores in log2 units) while it walks
 // quantized pages.
 struct WaveState {
   float m;        // running max (wave-uniform)
   float l;        // this lane's share of the running sum of weights
   float vmin;     // this lane's share of sum p_t * min_t over quantized tokens
-  // G = 128 (matrix-core pages): acc[0..3] digit-row sums of channel
-  // 16(lane>>4) + (lane&15), acc[4..7] of that channel + 64, full units.
-  // Other G: channel 16k + lane/4, slot quarter lane&3, half units.
+  // acc[0..3]: digit-row partial sums of channel 16(lane>>4) + (lane&15);
+  // acc[4..7]: those of that channel + 64
   float acc[8];
 };
 __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
@@ -108,122 +47,7 @@ __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
 }
 
 // ---------------------------------------------------------------------------
-// quantized pages
-// ---------------------------------------------------------------------------
-// Lane mapping inside a page (G tokens, d = 128 channels), quad = lanes 4i..4i+3:
-//   K: pass k covers tokens 16k..16k+15; quad i takes token 16k+i, lane 4i+j
-//      takes channels 32j..32j+31 (bytes 8j..8j+7 of the 32-byte code row).
-//   V: pass k covers channels 16k..16k+15; quad i takes channel 16k+i, lane
-//      4i+j takes slots (G/4)j..(G/4)j+G/4-1 (G/16 bytes of the channel row).
-template <int G>
-struct PageRegs {
-  static constexpr int KP = G / 16;       // K passes
-  static constexpr int VW = G / 64;       // V dwords per lane and channel (>= 1)
-  uint2 kc[KP];
-  uint32_t vc[8][VW];
-  uint32_t vm[KP / 4];  // V (min, scale) of this lane's tokens 16(4i+j)+ti
-  uint2 km;
-};
-
-// Loads in the order the page is consumed (K meta, K codes, V meta, V codes)
-// so that each wait only covers what the next step needs.
-template <int G>
-__device__ __forceinline__ void load_page(PageRegs<G>& r, const uint8_t* __restrict__ pg,
-                                          int lane) {
-  constexpr int KP = PageRegs<G>::KP, VW = PageRegs<G>::VW;
-  const int j = lane & 3, ti = lane >> 2;
-  r.km = ld_nt2(pg + kmeta_off(G) + 8 * lane);
-#pragma unroll
-  for (int k = 0; k < KP; ++k) r.kc[k] = ld_nt2(pg + (16 * k + ti) * (D / 4) + 8 * j);
-#pragma unroll
-  for (int i = 0; i < KP / 4; ++i) r.vm[i] = ld_nt1(pg + vmeta_off(G) + 4 * (16 * (4 * i + j) + ti));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint8_t* src = pg + vcode_off(G) + (16 * k + ti) * (G / 4) + j * (G / 16);
-    if constexpr (VW == 4) {
-      const uint4 t = ld_nt4(src);
-      r.vc[k][0] = t.x; r.vc[k][1] = t.y; r.vc[k][2] = t.z; r.vc[k][3] = t.w;
-    } else if constexpr (VW == 2) {
-      const uint2 t = ld_nt2(src);
-      r.vc[k][0] = t.x; r.vc[k][1] = t.y;
-    } else {
-      r.vc[k][0] = ld_nt1(src);
-    }
-  }
-}
-
-template <int G>
-__device__ __forceinline__ void compute_page(const PageRegs<G>& r, int n_valid, float qs0,
-                                             float qs1, float* qp, _Float16* ph, WaveState& st,
-                                             int lane) {
-  constexpr int KP = PageRegs<G>::KP, VW = PageRegs<G>::VW;
-  const int j = lane & 3, ti = lane >> 2;
-  // q'_c = q_c * scale_c (doubled for the code/2 view); bias = sum_c q_c * min_c
-  const float qa = 2.0f * qs0 * hi_f(r.km.x), qb = 2.0f * qs1 * hi_f(r.km.y);
-  const float bias = wave_sum(qs0 * lo_f(r.km.x) + qs1 * lo_f(r.km.y));
-  *reinterpret_cast<float2*>(qp + 2 * lane) = make_float2(qa, qb);
-  wave_lds_sync();
-
-  float z[KP];
-#pragma unroll
-  for (int k = 0; k < KP; ++k) z[k] = 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4* qv = reinterpret_cast<const float4*>(qp + 32 * j + 16 * h);
-    const float4 c0 = qv[0], c1 = qv[1], c2 = qv[2], c3 = qv[3];
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-      z[k] = dot16_codes(h ? r.kc[k].y : r.kc[k].x, c0, c1, c2, c3, z[k]);
-  }
-  // transpose-reduce inside the quad: afterwards lane j holds the full score
-  // of tokens 16(4i+j)+ti, i = 0..KP/4-1
-  constexpr int KT = KP / 4;
-  float za[KP / 2];
-#pragma unroll
-  for (int i = 0; i < KP / 2; ++i) {
-    const float keep = (j & 1) ? z[2 * i + 1] : z[2 * i];
-    const float send = (j & 1) ? z[2 * i] : z[2 * i + 1];
-    za[i] = keep + dpp<kQuadSwap1>(send);
-  }
-  float zt[KT];
-#pragma unroll
-  for (int i = 0; i < KT; ++i) {
-    const float keep = (j & 2) ? za[2 * i + 1] : za[2 * i];
-    const float send = (j & 2) ? za[2 * i] : za[2 * i + 1];
-    zt[i] = keep + dpp<kQuadSwap2>(send) + bias;
-  }
-  if (n_valid < G) {  // only a page built while the pool was filling is short
-#pragma unroll
-    for (int i = 0; i < KT; ++i)
-      if (16 * (4 * i + j) + ti >= n_valid) zt[i] = -INFINITY;
-  }
-  float mx = zt[0];
-#pragma unroll
-  for (int i = 1; i < KT; ++i) mx = fmaxf(mx, zt[i]);
-  mx = wave_max(mx);
-  if (mx == -INFINITY) return;  // a page without members
-  rescale_q(st, fmaxf(st.m, mx));
-#pragma unroll
-  for (int i = 0; i < KT; ++i) {
-    const float p = exp2_fast(zt[i] - st.m);
-    st.l += p;
-    st.vmin = fmaf(p, lo_f(r.vm[i]), st.vmin);
-    // p' = p * scale_t stays below 2^16 (p <= 1, scale <= 2^16 / 3) in fp16
-    ph[pair_slot(16 * (4 * i + j) + ti)] = _Float16(p * hi_f(r.vm[i]));
-  }
-  wave_lds_sync();
-#pragma unroll
-  for (int w = 0; w < VW; ++w) {
-    const uint4* pv = reinterpret_cast<const uint4*>(ph + j * (G / 4) + 16 * w);
-    const uint4 pa = pv[0], pb = pv[1];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) st.acc[k] = dot16_codes_h(r.vc[k][w], pa, pb, st.acc[k]);
-  }
-  wave_lds_sync();
-}
-
-// ---------------------------------------------------------------------------
-// quantized pages on the matrix cores (G = 128)
+// quantized pages on the matrix cores
 // ---------------------------------------------------------------------------
 // Both page products run on v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8
 // (E4M3) weight digits and B = the page's 2-bit codes read as FP4 (E2M1): with
@@ -314,32 +138,52 @@ __device__ __forceinline__ int mx_exp(float amax) {
   return max(__builtin_amdgcn_frexp_expf(amax), -100);
 }
 
+// Lane (j, g) of a page of G tokens: K tiles T = 0..G/16-1 (token 16T + j);
+// the lane's tokens are slots 16g + j + 64i, i < G/64; V k-blocks of 128 slots
+// (G = 64 leaves the upper half of the one block empty).
+template <int G>
 struct MxPage {
-  uint2 kc[8];     // K tile T: token 16T + j, channel items 32g..32g+31
-  uint2 vc[8];     // V tile C: channel 16C + j, slot items 32g..32g+31
-  uint32_t km[2];  // K (min, scale) of the lane's channels c0 and c0 + 2
-  uint32_t vm[2];  // V (min, scale) of the lane's slots 16g + j and 64 + 16g + j
+  static constexpr int NT = G / 16;              // K tiles
+  static constexpr int NZ = G / 64;              // tokens per lane
+  static constexpr int NB = (G + 127) / 128;     // V k-blocks
+  uint2 kc[NT];     // K tile T: token 16T + j, channel items 32g..32g+31
+  uint2 vc[8][NB];  // V tile C, block h: channel 16C + j, slots 128h + 32g + 0..31
+  uint32_t km[2];   // K (min, scale) of the lane's channels c0 and c0 + 2
+  uint32_t vm[NZ];  // V (min, scale) of the lane's slots
 };
 
-__device__ __forceinline__ void mx_load(MxPage& r, const uint8_t* __restrict__ pg, int lane,
+template <int G>
+__device__ __forceinline__ void mx_load(MxPage<G>& r, const uint8_t* __restrict__ pg, int lane,
                                         int c0) {
-  constexpr int G = 128;
+  using P = MxPage<G>;
   const int j = lane & 15, g = lane >> 4;
   r.km[0] = ld_nt1(pg + kmeta_off(G) + 4 * c0);
   r.km[1] = ld_nt1(pg + kmeta_off(G) + 4 * (c0 + 2));
 #pragma unroll
-  for (int T = 0; T < 8; ++T) r.kc[T] = ld_nt2(pg + (16 * T + j) * (D / 4) + 8 * g);
-  r.vm[0] = ld_nt1(pg + vmeta_off(G) + 4 * (16 * g + j));
-  r.vm[1] = ld_nt1(pg + vmeta_off(G) + 4 * (64 + 16 * g + j));
+  for (int T = 0; T < P::NT; ++T) r.kc[T] = ld_nt2(pg + (16 * T + j) * (D / 4) + 8 * g);
 #pragma unroll
-  for (int C = 0; C < 8; ++C) r.vc[C] = ld_nt2(pg + vcode_off(G) + (16 * C + j) * (G / 4) + 8 * g);
+  for (int i = 0; i < P::NZ; ++i) r.vm[i] = ld_nt1(pg + vmeta_off(G) + 4 * (16 * g + j + 64 * i));
+#pragma unroll
+  for (int C = 0; C < 8; ++C)
+#pragma unroll
+    for (int h = 0; h < P::NB; ++h) {
+      const uint8_t* row = pg + vcode_off(G) + (16 * C + j) * (G / 4);
+      if constexpr (G >= 128) {
+        r.vc[C][h] = ld_nt2(row + 32 * h + 8 * g);
+      } else {  // a 16-byte row: lane groups 2 and 3 have no slots
+        r.vc[C][h] = ld_nt2(row + 8 * (g & 1));
+        if (g >= 2) r.vc[C][h] = make_uint2(0u, 0u);
+      }
+    }
 }
 
-// One page. State layout: acc[0..3] are the digit-row partial sums of channel
-// 16g + j, acc[4..7] those of channel 64 + 16g + j (full units); the lane's
-// tokens are slots 16g + j and 64 + 16g + j.
-__device__ __forceinline__ void mx_page(const MxPage& r, int n_valid, float qs0, float qs1,
+// One page; the state's acc[0..3] and acc[4..7] are the digit-row sums of the
+// lane's channels 16g + j and 64 + 16g + j (full units).
+template <int G>
+__device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float qs0, float qs1,
                                         uint8_t* qa, uint8_t* pa, WaveState& st, int lane) {
+  using P = MxPage<G>;
+  constexpr int NZ = P::NZ, NB = P::NB;
   const int j = lane & 15, g = lane >> 4;
   // ---- scores: q'_c = q_c scale_c as digits, bias = sum_c q_c min_c
   const float qp0 = qs0 * hi_f(r.km[0]), qp1 = qs1 * hi_f(r.km[1]);
@@ -357,56 +201,79 @@ __device__ __forceinline__ void mx_page(const MxPage& r, int n_valid, float qs0,
   wave_lds_sync();
   const i32x8 aq = mx_a(qa, lane);
   const int sq = mx_scale(eq, lane);
-  f32x4v za = {0.f, 0.f, 0.f, 0.f}, zb = za;
-  za = mx_mfma<0>(aq, mx_b(r.kc[0]), za, sq);
-  zb = mx_mfma<0>(aq, mx_b(r.kc[4]), zb, sq);
-  za = mx_mfma<1>(aq, mx_b(r.kc[1]), za, sq);
-  zb = mx_mfma<1>(aq, mx_b(r.kc[5]), zb, sq);
-  za = mx_mfma<2>(aq, mx_b(r.kc[2]), za, sq);
-  zb = mx_mfma<2>(aq, mx_b(r.kc[6]), zb, sq);
-  za = mx_mfma<3>(aq, mx_b(r.kc[3]), za, sq);
-  zb = mx_mfma<3>(aq, mx_b(r.kc[7]), zb, sq);
+  f32x4v zr[NZ];
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) zr[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) zr[i] = mx_mfma<0>(aq, mx_b(r.kc[4 * i + 0]), zr[i], sq);
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) zr[i] = mx_mfma<1>(aq, mx_b(r.kc[4 * i + 1]), zr[i], sq);
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) zr[i] = mx_mfma<2>(aq, mx_b(r.kc[4 * i + 2]), zr[i], sq);
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) zr[i] = mx_mfma<3>(aq, mx_b(r.kc[4 * i + 3]), zr[i], sq);
   const int t0 = 16 * g + j;
-  float z0 = bias + ((za[0] + za[1]) + (za[2] + za[3]));
-  float z1 = bias + ((zb[0] + zb[1]) + (zb[2] + zb[3]));
-  if (n_valid < 128) {  // only a page built while the pool was filling is short
-    if (t0 >= n_valid) z0 = -INFINITY;
-    if (t0 + 64 >= n_valid) z1 = -INFINITY;
+  float z[NZ];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NZ; ++i) {
+    z[i] = bias + ((zr[i][0] + zr[i][1]) + (zr[i][2] + zr[i][3]));
+    if (n_valid < G && t0 + 64 * i >= n_valid) z[i] = -INFINITY;  // a short page
+    mx = fmaxf(mx, z[i]);
   }
-  const float mx = wave_max(fmaxf(z0, z1));
+  mx = wave_max(mx);
   if (mx == -INFINITY) return;  // a page without members
   rescale_q(st, fmaxf(st.m, mx));
-  const float p0 = exp2_fast(z0 - st.m), p1 = exp2_fast(z1 - st.m);
-  st.l += p0 + p1;
-  st.vmin = fmaf(p0, lo_f(r.vm[0]), fmaf(p1, lo_f(r.vm[1]), st.vmin));
   // ---- values: p'_t = p_t scale_t as digits
-  const float pp0 = p0 * hi_f(r.vm[0]), pp1 = p1 * hi_f(r.vm[1]);
-  const int ep = mx_exp(wave_max(fmaxf(pp0, pp1)));
-  {
-    float d0[4], d1[4];
-    mx_digits(pp0, ep, d0);
-    mx_digits(pp1, ep, d1);
-    const int kt = mx_k(t0);  // slot t0 + 64 sits at kt + 64
+  float pp[NZ];
+  float pmax = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(d0[k], d1[k], 0, false));
-      pa[128 * k + kt] = uint8_t(w);
-      pa[128 * k + kt + 64] = uint8_t(w >> 8);
+  for (int i = 0; i < NZ; ++i) {
+    const float p = exp2_fast(z[i] - st.m);
+    st.l += p;
+    st.vmin = fmaf(p, lo_f(r.vm[i]), st.vmin);
+    pp[i] = p * hi_f(r.vm[i]);
+    pmax = fmaxf(pmax, pp[i]);
+  }
+  const int ep = mx_exp(wave_max(pmax));
+  {
+    const int kt = mx_k(t0);  // slot t0 + 64i sits in block i/2 at kt + 64 (i & 1)
+#pragma unroll
+    for (int i = 0; i < NZ; i += 2) {
+      float d0[4], d1[4];
+      mx_digits(pp[i], ep, d0);
+      if (i + 1 < NZ) mx_digits(pp[i + 1], ep, d1);
+      uint8_t* blk = pa + 512 * (i / 2) + kt;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = uint32_t(
+            __builtin_amdgcn_cvt_pk_fp8_f32(d0[k], i + 1 < NZ ? d1[k] : 0.f, 0, false));
+        blk[128 * k] = uint8_t(w);
+        if (i + 1 < NZ) blk[128 * k + 64] = uint8_t(w >> 8);
+      }
     }
   }
   wave_lds_sync();
-  const i32x8 ap = mx_a(pa, lane);
+  i32x8 ap[NB];
+#pragma unroll
+  for (int h = 0; h < NB; ++h) ap[h] = mx_a(pa + 512 * h, lane);
+  if constexpr (G < 128) {  // logical k >= 64 has no slots
+    ap[0][4] = 0; ap[0][5] = 0; ap[0][6] = 0; ap[0][7] = 0;
+  }
   const int sp = mx_scale(ep, lane);
   f32x4v va = {st.acc[0], st.acc[1], st.acc[2], st.acc[3]};
   f32x4v vb = {st.acc[4], st.acc[5], st.acc[6], st.acc[7]};
-  va = mx_mfma<0>(ap, mx_b(r.vc[0]), va, sp);
-  vb = mx_mfma<0>(ap, mx_b(r.vc[4]), vb, sp);
-  va = mx_mfma<1>(ap, mx_b(r.vc[1]), va, sp);
-  vb = mx_mfma<1>(ap, mx_b(r.vc[5]), vb, sp);
-  va = mx_mfma<2>(ap, mx_b(r.vc[2]), va, sp);
-  vb = mx_mfma<2>(ap, mx_b(r.vc[6]), vb, sp);
-  va = mx_mfma<3>(ap, mx_b(r.vc[3]), va, sp);
-  vb = mx_mfma<3>(ap, mx_b(r.vc[7]), vb, sp);
+#pragma unroll
+  for (int h = 0; h < NB; ++h) {
+    va = mx_mfma<0>(ap[h], mx_b(r.vc[0][h]), va, sp);
+    vb = mx_mfma<0>(ap[h], mx_b(r.vc[4][h]), vb, sp);
+    va = mx_mfma<1>(ap[h], mx_b(r.vc[1][h]), va, sp);
+    vb = mx_mfma<1>(ap[h], mx_b(r.vc[5][h]), vb, sp);
+    va = mx_mfma<2>(ap[h], mx_b(r.vc[2][h]), va, sp);
+    vb = mx_mfma<2>(ap[h], mx_b(r.vc[6][h]), vb, sp);
+    va = mx_mfma<3>(ap[h], mx_b(r.vc[3][h]), va, sp);
+    vb = mx_mfma<3>(ap[h], mx_b(r.vc[7][h]), vb, sp);
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     st.acc[k] = va[k];
@@ -421,22 +288,23 @@ __device__ __forceinline__ void mx_page(const MxPage& r, int n_valid, float qs0,
 // Work-group = 4 waves on one (sequence, head, split). The waves deal the
 // split's pages round-robin, spread the fp16 chunks between their pages and
 // merge their states in LDS.
+template <int G>
 struct alignas(16) WaveLds {
-  float qp[D];          // q' of the current page
-  _Float16 ph[256];     // p' of the current page, pair layout (G <= 256)
-  float fin[4][D];      // fp16-path fold, then this wave's accumulator
+  uint8_t qa[4 * 128];                  // q' digit rows of the current page
+  uint8_t pa[MxPage<G>::NB * 4 * 128];  // p' digit rows, one block per 128 slots
+  float fin[4][D];                      // fp16-path fold, then this wave's accumulator
 };
 
-// G <= 128 fits 128 VGPRs (4 waves per SIMD); G = 256 keeps two waves per SIMD.
+// G <= 128 fits 128 VGPRs (4 waves per SIMD); G = 256 holds twice the codes.
 template <int G>
-__global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, const __half* __restrict__ q,
+__global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, const __half* __restrict__ q,
                                                      __half* __restrict__ out, int S,
                                                      HeadOrder order) {
-  __shared__ WaveLds lds_all[kWaves];
+  __shared__ WaveLds<G> lds_all[kWaves];
   __shared__ float mg_m[kWaves], mg_l[kWaves];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
-  WaveLds& L = lds_all[wave];
+  WaveLds<G>& L = lds_all[wave];
   const int s = blockIdx.x % S;
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);  // = b * H + h
   const int b = bh / a.Hkv;
@@ -453,14 +321,11 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
 
-  constexpr bool kMx = (G == 128);  // pages on the matrix cores
   const __half* qrow = q + size_t(bh) * D;
   const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
-  // the lane's two channels: 2 lane, 2 lane + 1, or for the matrix-core pages
-  // the channels of logical k = 2 lane, 2 lane + 1 (c0 and c0 + 2)
-  const int c0 = kMx ? mx_item(2 * lane) : 2 * lane;
-  const int c1 = kMx ? c0 + 2 : c0 + 1;
-  const float qs0 = __half2float(qrow[c0]) * qscale, qs1 = __half2float(qrow[c1]) * qscale;
+  // the lane's two channels: those of logical k = 2 lane, 2 lane + 1
+  const int c0 = mx_item(2 * lane);
+  const float qs0 = __half2float(qrow[c0]) * qscale, qs1 = __half2float(qrow[c0 + 2]) * qscale;
   WaveState st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -479,58 +344,38 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 2) void decode_kernel(Arena a, 
     fp16_chunk(src, chunk, min(kF16Chunk, t1 - chunk), q8, qscale, fs, lane);
     chunk += kWaves * kF16Chunk;
     // fold (m, l, acc) of the chunk into the page state; acc changes layout
-    // through LDS (channel 8*(lane&15)+e, row lane>>4 -> quad layout) and
-    // enters in half units
+    // through LDS (channel 8*(lane&15)+e, row lane>>4 -> the lane's channels
+    // 16(lane>>4) + (lane&15) and that + 64)
     const float M = fmaxf(st.m, fs.m);
     rescale_q(st, M);
     const float af = (fs.m == -INFINITY) ? 0.f : exp2_fast(fs.m - M);
     st.l = fmaf(fs.l, af, st.l);
-    const float ah = kMx ? af : 0.5f * af;
     float4* f = reinterpret_cast<float4*>(&L.fin[lane >> 4][8 * (lane & 15)]);
-    f[0] = make_float4(fs.acc[0] * ah, fs.acc[1] * ah, fs.acc[2] * ah, fs.acc[3] * ah);
-    f[1] = make_float4(fs.acc[4] * ah, fs.acc[5] * ah, fs.acc[6] * ah, fs.acc[7] * ah);
+    f[0] = make_float4(fs.acc[0] * af, fs.acc[1] * af, fs.acc[2] * af, fs.acc[3] * af);
+    f[1] = make_float4(fs.acc[4] * af, fs.acc[5] * af, fs.acc[6] * af, fs.acc[7] * af);
     wave_lds_sync();
-    if constexpr (kMx) {
-      const int ca = 16 * (lane >> 4) + (lane & 15);
-      st.acc[0] += (L.fin[0][ca] + L.fin[1][ca]) + (L.fin[2][ca] + L.fin[3][ca]);
-      st.acc[4] += (L.fin[0][ca + 64] + L.fin[1][ca + 64]) + (L.fin[2][ca + 64] + L.fin[3][ca + 64]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) st.acc[k] += L.fin[lane & 3][16 * k + (lane >> 2)];
-    }
+    const int ca = 16 * (lane >> 4) + (lane & 15);
+    st.acc[0] += (L.fin[0][ca] + L.fin[1][ca]) + (L.fin[2][ca] + L.fin[3][ca]);
+    st.acc[4] += (L.fin[0][ca + 64] + L.fin[1][ca + 64]) + (L.fin[2][ca + 64] + L.fin[3][ca + 64]);
     wave_lds_sync();
   };
   int n = 0;
   for (int u = sp.p0 + wave; u < p1; u += kWaves, ++n) {
     prio_by_work_left((p1 - u + kWaves - 1) / kWaves);
-    if constexpr (kMx) {
-      MxPage pr;
-      mx_load(pr, pages + size_t(u) * PB, lane, c0);
-      mx_page(pr, page_nvalid(a.G, a.P, u), qs0, qs1, reinterpret_cast<uint8_t*>(L.qp),
-              reinterpret_cast<uint8_t*>(L.ph), st, lane);
-    } else {
-      PageRegs<G> pr;
-      load_page<G>(pr, pages + size_t(u) * PB, lane);
-      compute_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qp, L.ph, st, lane);
-    }
+    MxPage<G> pr;
+    mx_load<G>(pr, pages + size_t(u) * PB, lane, c0);
+    mx_page<G>(pr, page_nvalid(a.G, a.P, u), qs0, qs1, L.qa, L.pa, st, lane);
     if ((n & 3) == wave && chunk < t1) next_chunk();
   }
   while (chunk < t1) next_chunk();
 
-  // this wave's state -> LDS in channel order (accumulator back to full units)
+  // this wave's state -> LDS in channel order
   const float l_tot = wave_sum(st.l);
   const float v_tot = wave_sum(st.vmin);
-  if constexpr (kMx) {
+  {
     const int ca = 16 * (lane >> 4) + (lane & 15);
     L.fin[0][ca] = ((st.acc[0] + st.acc[1]) + (st.acc[2] + st.acc[3])) + v_tot;
     L.fin[0][ca + 64] = ((st.acc[4] + st.acc[5]) + (st.acc[6] + st.acc[7])) + v_tot;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) st.acc[k] = quad_sum(st.acc[k]);
-    if ((lane & 3) == 0) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) L.fin[0][16 * k + (lane >> 2)] = fmaf(2.0f, st.acc[k], v_tot);
-    }
   }
   if (lane == 0) {
     mg_m[wave] = st.m;
