@@ -29,6 +29,7 @@ HBM_PEAK_GBS = 8000.0
 DECODE_SOURCES = ("decode_attention_ott_amd/csrc/ott_decode.hip",
                   "decode_attention_ott_amd/csrc/ott_decode_gqa.hip",
                   "decode_attention_ott_amd/csrc/ott_decode_common.h",
+                  "decode_attention_ott_amd/csrc/ott_mx.h",
                   "decode_attention_ott_amd/csrc/ott_device.h")
 
 
@@ -60,8 +61,8 @@ def decode_kernel_name(w) -> str:
     nq = w.num_q_heads // w.num_kv_heads
     if nq == 1:
         return f"decode_kernel<{w.group_size}>"
-    qb = 16 if nq % 16 == 0 else 8 if nq % 8 == 0 else 4 if nq % 4 == 0 else 2
-    return f"decode_gqa_kernel<{w.group_size},{qb}>"
+    na = 2 if nq % 8 == 0 else 1  # groups of 4 query heads per pass
+    return f"decode_gqa_kernel<{w.group_size}, {na}>"
 
 
 def kernel_source_hash() -> str:
@@ -133,6 +134,195 @@ def cpu_baseline(w, lengths, budget_s: float = 12.0):
             "s_per_step": full_step}
 
 
+def time_launches(launch, n_targets: int, stream, min_launches: int = 20) -> float:
+    """Median over 5 laps of the mean duration (us) of back-to-back launches,
+    launch(i) for i = 0, 1, ... round-robin over n_targets, timed with HIP events
+    on `stream` (the stream the kernels are launched on)."""
+    import torch
+    per_lap = n_targets * -(-min_launches // n_targets)
+    for i in range(n_targets):
+        launch(i)
+    laps = []
+    for _ in range(5):
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for i in range(per_lap):
+            launch(i % n_targets)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        laps.append(1e3 * d0.elapsed_time(d1) / per_lap)
+    return sorted(laps)[len(laps) // 2]
+
+
+def fp16_baseline(w, K, V, lens, qd, outd, stream) -> dict:
+    """The fp16 baseline decode (ott_fp16_decode) on the same K/V rows and lengths:
+    decode-only time and HBM rate. Algorithmic bytes: 512 per token and KV head
+    (K and V rows) plus 512 per query head (q in, out). One cache copy suffices:
+    a launch reads far more than the 256 MB Infinity Cache."""
+    import torch
+    from decode_attention_ott_amd import _lib as L
+    lens = [int(x) for x in lens]
+    max_len = max(lens)
+    dev = qd.device
+    Kd = torch.from_numpy(np.ascontiguousarray(K[:, :, :max_len])).to(dev)
+    Vd = torch.from_numpy(np.ascontiguousarray(V[:, :, :max_len])).to(dev)
+    nbytes = L.ott_fp16_decode_workspace(w.batch, w.num_q_heads, 256)
+    work = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+    sp = int(stream.cuda_stream)
+
+    def launch(_i):
+        L.ott_fp16_decode(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, Kd.data_ptr(),
+                          Vd.data_ptr(), max_len, lens, qd.data_ptr(), outd.data_ptr(), 0.0,
+                          work.data_ptr(), nbytes, 0, sp)
+    us = time_launches(launch, 1, stream)
+    nbytes_alg = 512 * w.num_kv_heads * sum(lens) + 512 * w.batch * w.num_q_heads
+    del Kd, Vd, work
+    torch.cuda.empty_cache()
+    nq = w.num_q_heads // w.num_kv_heads
+    hg = 8 if nq % 8 == 0 else 4 if nq % 4 == 0 else 2 if nq % 2 == 0 else 1
+    return {"kernel": f"fp16_decode_kernel<{hg}>", "decode_us": round(us, 2),
+            "alg_bytes_per_launch": int(nbytes_alg),
+            "achieved_gbs": round(nbytes_alg / (us * 1e-6) / 1e9, 1)}
+
+
+def sweep_batch(args, batches):
+    """OTT decode vs the fp16 baseline decode, decode-only, for each batch size
+    (the workload's shape otherwise): one JSON line per batch size."""
+    import torch
+    import synth
+    from decode_attention_ott_amd import OTTLayer, _lib as L
+    base = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    for B in batches:
+        w = base.with_(batch=B)
+        lengths = synth.prefill_lengths(w)
+        n_states = auto_states(w, lengths)
+        print(f"[sweep] batch {B}: generating inputs, {n_states} states", file=sys.stderr, flush=True)
+        K, V = synth.kv_all(w, int(lengths.max()) + 1)
+        Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+        layers = []
+        for _ in range(n_states):
+            lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()) + 1)
+            lay.prefill(Kd, Vd, lengths)
+            layers.append(lay)
+        del Kd, Vd
+        qd = torch.from_numpy(synth.queries(w, 0)).to(dev)
+        outd = torch.empty(B, w.num_q_heads, w.head_dim, dtype=torch.float16, device=dev)
+        ott_us = time_launches(lambda i: L.ott_decode(layers[i].handle, qd.data_ptr(),
+                                                      outd.data_ptr(), sp), n_states, stream)
+        ott_bytes = sum(algorithmic_decode_bytes(l) for l in layers) / n_states
+        del layers
+        torch.cuda.empty_cache()
+        fb = fp16_baseline(w, K, V, lengths, qd, outd, stream)
+        print(json.dumps({
+            "sweep": "batch", "workload": w.name, "batch": B,
+            "context": f"{w.prefill[0]}-{w.prefill[1]}",
+            "ott_decode_us": round(ott_us, 2), "ott_tokens_per_s": round(B / (ott_us * 1e-6), 1),
+            "ott_gbs": round(ott_bytes / (ott_us * 1e-6) / 1e9, 1),
+            "fp16_decode_us": fb["decode_us"],
+            "fp16_tokens_per_s": round(B / (fb["decode_us"] * 1e-6), 1),
+            "fp16_gbs": fb["achieved_gbs"],
+            "speedup": round(fb["decode_us"] / ott_us, 3)}), flush=True)
+
+
+def accuracy(args, batch: int = 8):
+    """Attention-output error of the OTT decode against exact attention over the
+    same fp16 tokens (the fp16 baseline kernel), for the plain 2-bit cache
+    (P = 0), the pages' pool size (P = 32) and a larger pool (P = 128), on the
+    workload's Key law and on its one-signed outlier-channel variant. The
+    workload's shape with `batch` sequences; one JSON line per setting."""
+    import torch
+    import synth
+    from decode_attention_ott_amd import OTTLayer, _lib as L
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    for one_signed in (False, True):
+        base = synth.WORKLOADS[args.workload].with_(batch=batch, one_signed=one_signed)
+        lengths = synth.prefill_lengths(base)
+        K, V = synth.kv_all(base, int(lengths.max()))
+        Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+        qd = torch.from_numpy(synth.queries(base, 0)).to(dev)
+        ref = torch.empty(batch, base.num_q_heads, base.head_dim, dtype=torch.float16, device=dev)
+        nbytes = L.ott_fp16_decode_workspace(batch, base.num_q_heads, 256)
+        work = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+        L.ott_fp16_decode(batch, base.num_q_heads, base.num_kv_heads, base.head_dim, Kd.data_ptr(),
+                          Vd.data_ptr(), int(lengths.max()), lengths, qd.data_ptr(), ref.data_ptr(),
+                          0.0, work.data_ptr(), nbytes, 0, sp)
+        r = ref.double()
+        for P in (0, 32, 128):
+            w = base.with_(pool_size=P)
+            lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()))
+            lay.prefill(Kd, Vd, lengths)
+            out = torch.empty_like(ref)
+            L.ott_decode(lay.handle, qd.data_ptr(), out.data_ptr(), sp)
+            torch.cuda.synchronize()
+            e = out.double() - r
+            rel = (e.norm(dim=-1) / r.norm(dim=-1)).flatten()
+            print(json.dumps({
+                "accuracy": "attention output vs exact fp16-cache attention",
+                "workload": w.name, "batch": batch, "one_signed_outlier_channels": one_signed,
+                "G": w.group_size, "R": w.residual, "P": P,
+                "rel_l2_total": round(float(e.norm() / r.norm()), 5),
+                "rel_l2_per_head_mean": round(float(rel.mean()), 5),
+                "rel_l2_per_head_max": round(float(rel.max()), 5),
+                "max_abs": round(float(e.abs().max()), 5)}), flush=True)
+            del lay
+        del Kd, Vd, work
+        torch.cuda.empty_cache()
+
+
+def sweep_params(args):
+    """OTT decode-only time for G, R and P varied one at a time around the
+    workload's values (G in {64, 128, 256}, R in {32, 64, 128}, P in {0, 32, 128}):
+    one JSON line per setting with the algorithmic bytes per quantized and per
+    cached token-head, decode time, tokens/s and the HBM fraction."""
+    import torch
+    import synth
+    from decode_attention_ott_amd import OTTLayer, _lib as L
+    base = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    lengths = synth.prefill_lengths(base)
+    K, V = synth.kv_all(base, int(lengths.max()) + 1)
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    del K, V
+    qd = torch.from_numpy(synth.queries(base, 0)).to(dev)
+    outd = torch.empty(base.batch, base.num_q_heads, base.head_dim, dtype=torch.float16, device=dev)
+    settings = [dict(group_size=g) for g in (64, 128, 256)]
+    settings += [dict(residual=r) for r in (64, 128)]
+    settings += [dict(pool_size=p) for p in (0, 128)]
+    for kw in settings:
+        w = base.with_(**kw)
+        n_states = auto_states(w, lengths)
+        print(f"[sweep] {kw}: {n_states} states", file=sys.stderr, flush=True)
+        layers = []
+        for _ in range(n_states):
+            lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()) + 1)
+            lay.prefill(Kd, Vd, lengths)
+            layers.append(lay)
+        us = time_launches(lambda i: L.ott_decode(layers[i].handle, qd.data_ptr(), outd.data_ptr(),
+                                                  sp), n_states, stream)
+        nbytes = sum(algorithmic_decode_bytes(l) for l in layers) / n_states
+        tokens = w.num_kv_heads * int(lengths.sum())
+        page = w.group_size * w.head_dim // 2 + 4 * w.head_dim + 4 * w.group_size
+        print(json.dumps({
+            "sweep": "params", "workload": w.name, "G": w.group_size, "R": w.residual,
+            "P": w.pool_size, "page_bytes": page,
+            "bytes_per_quantized_token_head": round(page / w.group_size, 2),
+            "bytes_per_cached_token_head": round(nbytes / tokens, 2),
+            "decode_us": round(us, 2), "tokens_per_s": round(w.batch / (us * 1e-6), 1),
+            "alg_bytes_per_launch": int(nbytes),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+        del layers
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +337,15 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before warm-up, one device-to-device copy of this many MiB; its "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings calibrate the counters")
+    ap.add_argument("--no-fp16-baseline", action="store_true",
+                    help="skip timing the fp16 baseline decode on the same K/V")
+    ap.add_argument("--sweep-batch", default="",
+                    help="comma-separated batch sizes: print OTT vs fp16 decode-only lines "
+                         "for each instead of the bench line")
+    ap.add_argument("--accuracy", action="store_true",
+                    help="print the OTT output error against exact attention for P = 0, 32, 128")
+    ap.add_argument("--sweep-params", action="store_true",
+                    help="print OTT decode-only lines for G, R and P varied one at a time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this OTT build has no multi-GPU path "
@@ -158,6 +357,15 @@ def main():
     import synth
     from decode_attention_ott_amd import OTTLayer, _lib as L
 
+    if args.accuracy:
+        accuracy(args)
+        return
+    if args.sweep_params:
+        sweep_params(args)
+        return
+    if args.sweep_batch:
+        sweep_batch(args, [int(x) for x in args.sweep_batch.split(",")])
+        return
     w = synth.WORKLOADS[args.workload]
     lengths = synth.prefill_lengths(w)
     if args.states <= 0:
@@ -227,24 +435,12 @@ def main():
     # The decode alone, launched back to back over the states (state is not
     # modified by a decode): 5 laps of >= 20 launches each, the median lap's
     # per-launch duration is the figure the roofline uses.
-    per_lap = args.states * -(-20 // args.states)
     dec_bytes = [algorithmic_decode_bytes(lay) for lay in layers]
     q_last = qd[args.warmup + args.steps - 1]
-    for i in range(args.states):
-        L.ott_decode(layers[i].handle, q_last.data_ptr(), outd.data_ptr(), sp)
-    laps = []
-    for lap in range(5):
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        d0.record(stream)
-        for i in range(per_lap):
-            L.ott_decode(layers[i % args.states].handle, q_last.data_ptr(), outd.data_ptr(), sp)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        laps.append(1e3 * d0.elapsed_time(d1) / per_lap)
-    dec_only_us = sorted(laps)[len(laps) // 2]
-    n_dec = 5 * per_lap
+    dec_only_us = time_launches(
+        lambda i: L.ott_decode(layers[i].handle, q_last.data_ptr(), outd.data_ptr(), sp),
+        args.states, stream)
+    n_dec = 5 * args.states * -(-20 // args.states)
     bytes_per_launch = sum(dec_bytes) / len(dec_bytes)
     achieved = bytes_per_launch / (dec_only_us * 1e-6) / 1e9
     traffic = load_traffic(w.name)
@@ -255,6 +451,15 @@ def main():
                 "decode_us": round(dec_only_us, 2),
                 "decode_launches": n_dec,
                 "alg_bytes_per_launch": int(bytes_per_launch)}
+    fp16 = None
+    if not args.no_fp16_baseline:
+        print("[bench] timing the fp16 baseline decode", file=sys.stderr, flush=True)
+        # the lengths the OTT states hold at the timed decodes
+        lens_now = [layers[0].seq_state(b)[0] for b in range(w.batch)]
+        del layers
+        torch.cuda.empty_cache()
+        fp16 = fp16_baseline(w, K, V, lens_now, q_last, outd, stream)
+        fp16["speedup_ott_vs_fp16"] = round(fp16["decode_us"] / dec_only_us, 3)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -269,7 +474,7 @@ def main():
                       "R": w.residual, "P": w.pool_size, "states": args.states,
                       "splits": args.splits or "auto",
                       "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window"},
-           "roofline": roofline, "cpu_baseline": cpu}
+           "roofline": roofline, "cpu_baseline": cpu, "fp16_baseline": fp16}
     print(json.dumps(res), flush=True)
 
 

@@ -5,13 +5,14 @@ C ABI in include/ott.h. This package is its Python binding: ``_lib`` holds the
 ctypes calls under the C names, ``OTTLayer`` wraps one layer's arena.
 """
 from . import _lib
-from ._lib import (OttError, ott_append, ott_decode, ott_destroy, ott_get_layout,
+from ._lib import (OttError, ott_append, ott_decode, ott_destroy, ott_fp16_decode,
+                   ott_fp16_decode_workspace, ott_get_layout,
                    ott_get_seq_state, ott_init, ott_quantize_group, ott_set_num_splits,
                    ott_status_string)
 
 __all__ = ["OTTLayer", "OttError", "ott_init", "ott_append", "ott_quantize_group", "ott_decode",
            "ott_destroy", "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits",
-           "ott_status_string"]
+           "ott_status_string", "ott_fp16_decode", "ott_fp16_decode_workspace"]
 
 
 def __getattr__(name):

@@ -22,7 +22,8 @@ STATUS_NAMES = {
 
 # Every symbol include/ott.h declares.
 EXPORTS = ("ott_init", "ott_append", "ott_quantize_group", "ott_decode", "ott_destroy",
-           "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits", "ott_status_string")
+           "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits", "ott_status_string",
+           "ott_fp16_decode", "ott_fp16_decode_workspace")
 
 
 class ott_config_t(ctypes.Structure):
@@ -71,6 +72,11 @@ def _load() -> ctypes.CDLL:
     lib.ott_get_seq_state.restype = ctypes.c_int
     lib.ott_set_num_splits.argtypes = [H, I32]
     lib.ott_set_num_splits.restype = ctypes.c_int
+    lib.ott_fp16_decode.argtypes = [I32, I32, I32, I32, VP, VP, I32, P(I32), VP, VP, ctypes.c_float,
+                                    VP, ctypes.c_size_t, I32, VP]
+    lib.ott_fp16_decode.restype = ctypes.c_int
+    lib.ott_fp16_decode_workspace.argtypes = [I32, I32, I32]
+    lib.ott_fp16_decode_workspace.restype = ctypes.c_size_t
     lib.ott_status_string.argtypes = [ctypes.c_int]
     lib.ott_status_string.restype = ctypes.c_char_p
     return lib
@@ -146,3 +152,17 @@ def ott_set_num_splits(h, s: int) -> None:
 
 def ott_status_string(status: int) -> str:
     return lib.ott_status_string(status).decode()
+
+
+def ott_fp16_decode(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, d_k: int,
+                    d_v: int, max_len: int, lens, d_q: int, d_out: int, sm_scale: float,
+                    d_work: Optional[int], work_bytes: int, num_splits: int, stream: int) -> None:
+    arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+    _check(lib.ott_fp16_decode(batch, num_q_heads, num_kv_heads, head_dim, ctypes.c_void_p(d_k),
+                               ctypes.c_void_p(d_v), max_len, arr, ctypes.c_void_p(d_q),
+                               ctypes.c_void_p(d_out), sm_scale, ctypes.c_void_p(d_work),
+                               work_bytes, num_splits, ctypes.c_void_p(stream)), "ott_fp16_decode")
+
+
+def ott_fp16_decode_workspace(batch: int, num_q_heads: int, num_splits: int) -> int:
+    return int(lib.ott_fp16_decode_workspace(batch, num_q_heads, num_splits))

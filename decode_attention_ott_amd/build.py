@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libott.so")
-SOURCES = ["ott_api.cpp", "ott_update.hip", "ott_decode.hip", "ott_decode_gqa.hip"]
+SOURCES = ["ott_api.cpp", "ott_update.hip", "ott_decode.hip", "ott_decode_gqa.hip", "ott_fp16_decode.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are switched off for all device code (hipcc forwards the

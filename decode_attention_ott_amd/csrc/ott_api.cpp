@@ -43,7 +43,7 @@ ott_status_t validate_config(const ott_config_t* c) {
     return OTT_ERR_UNSUPPORTED;
   if (c->pool_size > 512 || c->residual > 4096) return OTT_ERR_UNSUPPORTED;
   const int nq = c->num_q_heads / c->num_kv_heads;
-  if (!(nq == 1 || nq == 2 || nq % 4 == 0) || nq > 64) return OTT_ERR_UNSUPPORTED;
+  if (nq > 64) return OTT_ERR_UNSUPPORTED;
   const int64_t heads = int64_t(c->batch) * c->num_kv_heads;
   if (heads > (1 << 20)) return OTT_ERR_UNSUPPORTED;
   return OTT_OK;
@@ -316,6 +316,67 @@ ott_status_t ott_set_num_splits(ott_handle_t h, int32_t num_splits) {
   if (!h || num_splits < 0 || num_splits > h->lay.max_splits) return OTT_ERR_INVALID_ARG;
   h->forced_splits = num_splits;
   return OTT_OK;
+}
+
+size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_splits <= 1) return 0;
+  return size_t(batch) * num_q_heads * num_splits * (2 + ott::kHeadDim) * sizeof(float);
+}
+
+ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, const void* d_k, const void* d_v, int32_t max_len,
+                             const int32_t* h_len, const void* d_q, void* d_out, float sm_scale,
+                             void* d_work, size_t work_bytes, int32_t num_splits, void* stream) {
+  if (batch < 1 || batch > ott::kMaxBatch || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+      num_q_heads % num_kv_heads != 0 || max_len < 1 || num_splits < 0 || !h_len)
+    return OTT_ERR_INVALID_ARG;
+  if (head_dim != ott::kHeadDim) return OTT_ERR_UNSUPPORTED;
+  if (!d_k || !d_v || !d_q || !d_out) return OTT_ERR_INVALID_ARG;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(d_k) || misaligned(d_v) || misaligned(d_q) || misaligned(d_out))
+    return OTT_ERR_INVALID_ARG;
+  ott::Fp16Lens lens;
+  int32_t lmax = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (h_len[b] < 1 || h_len[b] > max_len) return OTT_ERR_STATE;
+    lens.len[b] = h_len[b];
+    lmax = std::max(lmax, h_len[b]);
+  }
+  // splits: as given, or enough work-groups for one round of the GPU with at
+  // least 256 tokens each; never more than the workspace holds
+  const int64_t fit = (d_work == nullptr)
+                          ? 1
+                          : int64_t(work_bytes / (size_t(batch) * num_q_heads * (2 + ott::kHeadDim) *
+                                                  sizeof(float)));
+  int S = num_splits;
+  if (S == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    int wpc = ott::fp16_decode_wgs_per_cu(num_q_heads / num_kv_heads);
+    if (wpc <= 0) wpc = 2;
+    S = int(std::max<int64_t>(1, int64_t(cus) * wpc / (int64_t(batch) * num_kv_heads)));
+    S = int(std::min<int64_t>(S, std::max<int64_t>(1, (lmax + 255) / 256)));
+    S = int(std::min<int64_t>(S, std::max<int64_t>(1, fit)));
+  } else if (S > 1 && S > fit) {
+    return OTT_ERR_ARENA_TOO_SMALL;
+  }
+  ott::Fp16Cache c;
+  c.k = static_cast<const __half*>(d_k);
+  c.v = static_cast<const __half*>(d_v);
+  c.q = static_cast<const __half*>(d_q);
+  c.out = static_cast<__half*>(d_out);
+  c.part = static_cast<float*>(d_work);
+  c.B = batch;
+  c.Hq = num_q_heads;
+  c.Hkv = num_kv_heads;
+  c.max_len = max_len;
+  c.sm_scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(head_dim));
+  return ott::launch_fp16_decode(c, lens, S, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? OTT_OK
+             : OTT_ERR_HIP;
 }
 
 const char* ott_status_string(ott_status_t s) {

@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "ott_decode_common.h"
+#include "ott_mx.h"
 
 namespace ott {
 namespace {
@@ -49,26 +50,8 @@ __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
 // ---------------------------------------------------------------------------
 // quantized pages on the matrix cores
 // ---------------------------------------------------------------------------
-// Both page products run on v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8
-// (E4M3) weight digits and B = the page's 2-bit codes read as FP4 (E2M1): with
-// its two high bits cleared, a code nibble is the FP4 value code/2, so a code
-// dword becomes two B dwords with two masks and no conversion.
-//
-// Operand layout of that instruction (lane l, j = l & 15, g = l >> 4):
-//   B: column j; byte-nibble n of dword w is logical k = 32g + 8w + n.
-//   A: row j; byte b is logical k = 16g + (b & 15) + 64 (b >> 4).
-//   D: column j, rows 4g..4g+3 in the four result registers.
-//   The E8M0 scale of A row r for k-block kb is the op_sel byte of lane r+16kb.
-// The lane's B chunk is 8 code bytes (32 items, item 4i+h at bits 2h of byte
-// i); after the masks, logical k holds item mx_item(k) of the page row.
-//
-// Exactness: the matrix core sums one instruction's products with a limited
-// number of bits below the largest, so every weight is split into 4
-// fixed-point digits in [-16, 16] relative to one power of two 2^e per page
-// and kind (digit k has step 2^(e-4-5k)). A row of digits times code/2 gives
-// products on one grid of half-steps, at most 24 steps each, whose sums are
-// exact; the step enters as the row's E8M0 scale. 4 digits keep 19 bits of the
-// largest weight of the page.
+// The page products run on the fp8 x fp4 matrix cores (helpers and exactness
+// argument in ott_mx.h).
 //
 // Rows: A holds the 4 digit rows of the page four times (rows 4i..4i+3). The
 // scale register packs one byte per replica; byte i is the real scale for
@@ -76,46 +59,6 @@ __device__ __forceinline__ void rescale_q(WaveState& st, float m_new) {
 // Tiles 0..3 accumulate into one result and 4..7 into another, so lane group g
 // ends with exactly its own tiles g and g+4 (the masked products add at most
 // 2^-110 in total).
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-constexpr uint32_t kCodeMask = 0x33333333u;
-
-// item of logical k (channel for K, slot for V), and its inverse
-__device__ __forceinline__ int mx_item(int k) {
-  return (k & ~31) | (k & 16) | ((k >> 3) & 1) | ((k & 7) << 1);
-}
-__device__ __forceinline__ int mx_k(int t) {
-  return (t & ~31) | (t & 16) | ((t & 1) << 3) | ((t & 15) >> 1);
-}
-
-__device__ __forceinline__ i32x8 mx_b(uint2 c) {
-  i32x8 b;
-  b[0] = int(c.x & kCodeMask);
-  b[1] = int((c.x >> 2) & kCodeMask);
-  b[2] = int(c.y & kCodeMask);
-  b[3] = int((c.y >> 2) & kCodeMask);
-  b[4] = 0;
-  b[5] = 0;
-  b[6] = 0;
-  b[7] = 0;
-  return b;
-}
-
-template <int SEL>
-__device__ __forceinline__ f32x4v mx_mfma(const i32x8& a, const i32x8& b, const f32x4v& c, int sc) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0 /* A: fp8 e4m3 */,
-                                                          4 /* B: fp4 e2m1 */, SEL, sc, 0, 127);
-}
-
-// x = sum_k d[k] 2^(e-4-5k) + r with |r| <= 2^(e-20), given |x| < 2^e
-__device__ __forceinline__ void mx_digits(float x, int e, float (&d)[4]) {
-  float r = __builtin_amdgcn_ldexpf(x, 4 - e);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    d[k] = __builtin_rintf(r);
-    r = (r - d[k]) * 32.0f;
-  }
-}
 
 // A operand: digit row (lane & 3) of a [4][128] byte block in logical k order
 __device__ __forceinline__ i32x8 mx_a(const uint8_t* rows, int lane) {
@@ -134,9 +77,6 @@ __device__ __forceinline__ int mx_scale(int e, int lane) {
   return (124 - 5 * (lane & 3) + e) << (8 * ((lane >> 2) & 3));
 }
 
-__device__ __forceinline__ int mx_exp(float amax) {
-  return max(__builtin_amdgcn_frexp_expf(amax), -100);
-}
 
 // Lane (j, g) of a page of G tokens: K tiles T = 0..G/16-1 (token 16T + j);
 // the lane's tokens are slots 16g + j + 64i, i < G/64; V k-blocks of 128 slots
@@ -408,42 +348,12 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   }
 }
 
-// Merge of S split partial states per (sequence, query head): the partials
-// are read 16 at a time with all loads in flight, then merged online
-// (M, L, A) <- (max, L e^(M-M') + sum l e^(m-M'), A e^(M-M') + sum acc e^(m-M')).
+// Merge of the S split partial states of each (sequence, query head).
 __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict__ out, int S) {
-  constexpr int kChunk = 16;
   const int bq = blockIdx.x;  // b * Hq + qh
-  const int c = threadIdx.x;
   const float* part = reinterpret_cast<const float*>(a.base + a.off_partials) +
                       size_t(bq) * a.max_splits * (2 + D);
-  float M = -INFINITY, Ls = 0.f, A = 0.f;
-  for (int i0 = 0; i0 < S; i0 += kChunk) {
-    float m[kChunk], l[kChunk], v[kChunk];
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const bool ok = i0 + k < S;
-      const float* p = part + size_t(ok ? i0 + k : 0) * (2 + D);
-      m[k] = ok ? p[0] : -INFINITY;
-      l[k] = p[1];
-      v[k] = p[2 + c];
-    }
-    float Mc = M;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
-    if (Mc == -INFINITY) continue;
-    const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mc);
-    Ls *= f0;
-    A *= f0;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const float f = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mc);
-      Ls = fmaf(l[k], f, Ls);
-      A = fmaf(v[k], f, A);
-    }
-    M = Mc;
-  }
-  out[size_t(bq) * D + c] = __float2half_rn(A / Ls);
+  out[size_t(bq) * D + threadIdx.x] = __float2half_rn(merge_partials(part, S, threadIdx.x));
 }
 
 }  // namespace

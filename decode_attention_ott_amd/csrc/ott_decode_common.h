@@ -259,5 +259,40 @@ __device__ __forceinline__ float* partial_ptr(const Arena& a, int b, int qh, int
          ((size_t(b) * a.Hq + qh) * a.max_splits + s) * (2 + D);
 }
 
+// Channel c of the merged output of S partial states {m, l, acc[D]} (log2
+// units) stored at part + s * (2 + D): the partials are read 16 at a time with
+// every load in flight, then merged online,
+// (M, L, A) <- (M', L e^(M-M') + sum l e^(m-M'), A e^(M-M') + sum acc e^(m-M')).
+__device__ __forceinline__ float merge_partials(const float* __restrict__ part, int S, int c) {
+  constexpr int kChunk = 16;
+  float M = -INFINITY, Ls = 0.f, A = 0.f;
+  for (int i0 = 0; i0 < S; i0 += kChunk) {
+    float m[kChunk], l[kChunk], v[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const bool ok = i0 + k < S;
+      const float* p = part + size_t(ok ? i0 + k : 0) * (2 + D);
+      m[k] = ok ? p[0] : -INFINITY;
+      l[k] = p[1];
+      v[k] = p[2 + c];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
+    if (Mc == -INFINITY) continue;
+    const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mc);
+    Ls *= f0;
+    A *= f0;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float f = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mc);
+      Ls = fmaf(l[k], f, Ls);
+      A = fmaf(v[k], f, A);
+    }
+    M = Mc;
+  }
+  return A / Ls;
+}
+
 }  // namespace dec
 }  // namespace ott

@@ -1,404 +1,301 @@
 // Decoding stage for grouped query heads (several query heads per KV head) on
-// gfx950 matrix cores.
+// the gfx950 fp8 x fp4 matrix cores.
 //
 // Same computation as the one-head kernel ([Blog] zijie-tian.site summary,
 // section 3.3 flowchart; [Abs] sciencestack.ai, Figure 2 top): scores of the
 // quantized Keys, the window Keys and the pool Keys go under one softmax and
-// the weights multiply the matching Values. With QB query heads sharing a
-// page, both products over the page are small dense contractions:
+// the weights multiply the matching Values. The query heads that share a page
+// make both products over it small dense contractions:
 //
-//   scores  z[h][t] = bias[h] + sum_c q'[h][c] * kcode[t][c]   (QB x 128 x G)
-//   values  o[h][c] += sum_t p'[h][t] * vcode[c][t]            (QB x G x 128)
+//   scores  z[h][t] = bias[h] + sum_c q'[h][c] * kcode[t][c]
+//   values  o[h][c] += sum_t p'[h][t] * vcode[c][t]
 //
-// with q'[h][c] = qs[h][c] * scale_c and p'[h][t] = p[h][t] * scale_t. Both
-// run on v_mfma_f32_16x16x32_f16. A 2-bit code whose two high neighbour bits
-// are masked off is the FP4 (E2M1) value code/2, which one conversion per two
-// codes turns into fp16 (0, 0.5, 1, 1.5: exact and normal); the factor 2
-// returns after the products. q' enters as an fp16 pair hi + lo (22
-// significant bits), p' as one fp16 value.
+// with q'[h][c] = qs[h][c] * scale_c and p'[h][t] = p[h][t] * scale_t. Both run
+// on v_mfma_scale_f32_16x16x128_f8f6f4 (operand layouts and the exactness of
+// fixed-point digit rows in ott_mx.h): a group of 4 query heads fills the 16 A
+// rows with 4 digit rows per head (row 4h + k = digit k of head h, each row
+// with its own E8M0 scale), and the 2-bit codes are the B operand as FP4.
+// Result row 4h + k then sits in lane group h, so every lane group owns one
+// head of the group: its scores, its softmax state and its value sums.
+//
+// Token order of the score tiles. Column j of K tile T (block b = T / NTB,
+// t = T % NTB) is the token of logical slot k = NTB j + t of value block b, so
+// a lane's NTB scores are NTB consecutive logical slots of the value operand:
+// each digit row of p' leaves the lane as one 8-byte (G >= 128) or 4-byte
+// (G = 64) LDS write.
 #include "ott_decode_common.h"
+#include "ott_mx.h"
 
 namespace ott {
 namespace {
 using namespace dev;
 using namespace dec;
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned u4v __attribute__((ext_vector_type(4)));
-
-// D(16x16) += A(16x32) B(32x16). Lane l holds A row l%16, B column l%16, the
-// k-slots 8(l/16)..8(l/16)+7 of both, and D rows 4(l/16)..4(l/16)+3 of column
-// l%16.
-__device__ __forceinline__ f4 mfma16(const h8& a, const h8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// One dword of 16 codes (code n in bits 2n..2n+1) as the B operands of two
-// MFMA steps, as code/2: slot e of step h holds code 8h + kPerm[e] (each FP4
-// conversion yields codes 0 and 2, or 1 and 3, of one byte).
-__device__ __forceinline__ void codes_b(uint32_t w, h8& b0, h8& b1) {
-  const uint32_t ev = w & 0x33333333u;         // codes 0 and 2 of every byte
-  const uint32_t od = (w >> 2) & 0x33333333u;  // codes 1 and 3 of every byte
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0);
-  const h2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0);
-  const h2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1);
-  const h2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1);
-  const h2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2);
-  const h2 o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2);
-  const h2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3);
-  const h2 o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3);
-  b0 = h8{e0[0], e0[1], o0[0], o0[1], e1[0], e1[1], o1[0], o1[1]};
-  b1 = h8{e2[0], e2[1], o2[0], o2[1], e3[0], e3[1], o3[0], o3[1]};
-}
-
-// Code (channel or token) offset of slot e inside an MFMA step.
-__host__ __device__ constexpr int kPerm(int e) { return (e & ~3) | ((e & 1) << 1) | ((e >> 1) & 1); }
-
-// Shapes for page size G and QB query heads per pass.
-//   K: tile T = tokens 16T..16T+15 (B column = token); lane group g covers
-//      channels 32g..32g+31 of the token's code row, step cb the channels
-//      32g + 8cb + kPerm(slot).
-//   V: tile ct = channels 16ct..16ct+15 (B column = channel); lane group g
-//      covers tokens g*G/4..g*G/4+G/4-1 of the channel's code row, step kb the
-//      tokens g*G/4 + 8kb + kPerm(slot).
-//   A rows: query head h at row h (its q' hi part and p'), q' lo part at row
-//      QB + h; with QB = 16 the lo parts fill a second 16-row array.
-template <int G, int QB>
-struct Geo {
-  static constexpr int NA = QB <= 8 ? 1 : 2;       // 16-row arrays of q'
-  static constexpr int ZR = QB <= 8 ? 2 * QB : QB;  // score values kept per token
-  static constexpr int KT = G / 16;                 // K tiles
-  static constexpr int VDW = G / 64;                // V code dwords per lane and channel
-  static constexpr int KB = G / 32;                 // V steps
-  static constexpr int NP = G / 2;                  // token pairs (t, t + 2)
-  static constexpr int PPL = (NP + 63) / 64;        // pairs per lane
-  static constexpr int QPL = (QB + 3) / 4;          // query heads per lane in the q' step
-  static constexpr int ZS0 = G * ZR > 4 * D ? G * ZR : 4 * D;
-  static constexpr int ZS = ZS0 > QB * D ? ZS0 : QB * D;  // floats
-  // A operands live in blocks of 16 rows x 16 bytes, padded to 272 bytes so
-  // that writes of one row across blocks spread over the LDS banks
-  static constexpr int kBlk = 272;
-  static constexpr int NBLK = NA * 16 > KB * 4 ? NA * 16 : KB * 4;
-};
-
-// First token of pair pi; the pair is (t, t + 2) and fills the dword p (slots
-// 2p, 2p + 1) of A row h in V step kb for lane group g.
 template <int G>
-__device__ __forceinline__ int pair_token(int pi) {
-  const int g = pi / (G / 8), rem = pi % (G / 8), kb = rem >> 2, p = rem & 3;
-  return g * (G / 4) + 8 * kb + (p & 1) + 4 * (p >> 1);
-}
-
-template <int G, int QB>
-struct alignas(16) GqaLds {
-  // q' A operands: block (a * 4 + cb) * 4 + lane group; p' A operands: block kb * 4 + lane group
-  uint8_t ab[Geo<G, QB>::NBLK * Geo<G, QB>::kBlk];
-  float zs[Geo<G, QB>::ZS];  // page scores [token][row]; fp16 fold; final state
-  float bias[16];
-  __device__ __forceinline__ h8* row(int blk, int r) {
-    return reinterpret_cast<h8*>(ab + blk * Geo<G, QB>::kBlk + 16 * r);
-  }
+struct Gx {
+  static constexpr int NB = (G + 127) / 128;         // value k-blocks of 128 slots
+  static constexpr int NTB = G >= 128 ? 8 : G / 16;  // score tiles per block
+  static constexpr int NT = G / 16;                  // score tiles
+  static constexpr int RS = 144;                     // LDS bytes per A row (128 + pad)
+  static constexpr int ABLK = 16 * RS;               // one A operand block
 };
 
-template <int QB>
-struct GqaState {
-  float m[QB];     // running max per query head (wave-uniform)
-  float l[QB];     // this lane's share of the running sums
-  float vmin[QB];  // this lane's share of sum p_t * min_t
-  f4 acc[8];       // sum p'_t c_t / 2: rows 4(lane>>4)+r, channel 16ct + (lane&15)
-};
-
-// Per-lane value of a per-head array for D row 4g + r.
-template <int QB>
-__device__ __forceinline__ float row_pick(const float (&v)[QB], int g, int r) {
-  float x = v[r % QB];
-#pragma unroll
-  for (int gg = 1; gg < (QB + 3) / 4; ++gg)
-    if (g % ((QB + 3) / 4) == gg) x = v[4 * gg + r];
-  return x;
-}
-
-// Wave-wide maxima of N values per lane, the N reductions in lockstep.
-template <int N>
-__device__ __forceinline__ void wave_max_n(float (&x)[N]) {
-#pragma unroll
-  for (int h = 0; h < N; ++h) x[h] = fmaxf(x[h], dpp<kQuadSwap1>(x[h]));
-#pragma unroll
-  for (int h = 0; h < N; ++h) x[h] = fmaxf(x[h], dpp<kQuadSwap2>(x[h]));
-#pragma unroll
-  for (int h = 0; h < N; ++h) x[h] = fmaxf(x[h], dpp<kHalfMirror>(x[h]));
-#pragma unroll
-  for (int h = 0; h < N; ++h) x[h] = fmaxf(x[h], dpp<kRowMirror>(x[h]));
-#pragma unroll
-  for (int h = 0; h < N; ++h) {
-    const f32x2 p = swap16(x[h]);
-    x[h] = fmaxf(p.x, p.y);
-  }
-#pragma unroll
-  for (int h = 0; h < N; ++h) {
-    const f32x2 p = swap32(x[h]);
-    x[h] = fmaxf(p.x, p.y);
-  }
+// token of score tile T, column j
+template <int G>
+__device__ __forceinline__ int gx_token(int T, int j) {
+  constexpr int NTB = Gx<G>::NTB;
+  return 128 * (T / NTB) + mx_item(NTB * j + T % NTB);
 }
 
 // The part of a page one lane reads from memory.
 template <int G>
-struct GqaPage {
-  static constexpr int KT = G / 16, VDW = G / 64, PPL = (G / 2 + 63) / 64;
-  uint4 kmA, kmB;        // K (min, scale) of the lane's q' channels 8j..8j+7
-  uint2 kc[KT];          // K codes: tile T, token 16T + (lane&15), lane group's 32 channels
-  uint32_t vm[PPL][2];   // V (min, scale) of the lane's token pairs
-  uint32_t vc[8][VDW];   // V codes: tile ct, channel 16ct + (lane&15), lane group's tokens
+struct GxPage {
+  static constexpr int NT = Gx<G>::NT, NB = Gx<G>::NB;
+  uint4 km[2];         // K (min, scale) of channels 8(lane&15)..+7
+  uint2 kc[NT];        // K codes: tile T, token gx_token(T, lane&15), channels 32g..32g+31
+  uint32_t vm[NT];     // V (min, scale) of the lane's tokens
+  uint2 vc[8][NB];     // V codes: channel 16C + (lane&15), slots 128h + 32g..+31
 };
 
 template <int G>
-__device__ __forceinline__ void gqa_load(GqaPage<G>& r, const uint8_t* __restrict__ pg, int lane) {
-  constexpr int NP = G / 2;
+__device__ __forceinline__ void gx_load(GxPage<G>& r, const uint8_t* __restrict__ pg, int lane) {
+  constexpr int NT = Gx<G>::NT, NB = Gx<G>::NB;
   const int j = lane & 15, g = lane >> 4;
-  const int c0 = 8 * j;  // q' chunk of this lane: channels c0..c0+7 (lane group j>>2, step j&3)
-  r.kmA = ld_nt4(pg + kmeta_off(G) + 4 * c0);
-  r.kmB = ld_nt4(pg + kmeta_off(G) + 4 * (c0 + 4));
+  r.km[0] = ld_nt4(pg + kmeta_off(G) + 32 * j);
+  r.km[1] = ld_nt4(pg + kmeta_off(G) + 32 * j + 16);
 #pragma unroll
-  for (int T = 0; T < GqaPage<G>::KT; ++T) r.kc[T] = ld_nt2(pg + (16 * T + j) * (D / 4) + 8 * g);
+  for (int T = 0; T < NT; ++T) r.kc[T] = ld_nt2(pg + gx_token<G>(T, j) * (D / 4) + 8 * g);
 #pragma unroll
-  for (int k = 0; k < GqaPage<G>::PPL; ++k) {
-    const int t0 = pair_token<G>(min(lane + 64 * k, NP - 1));
-    r.vm[k][0] = ld_nt1(pg + vmeta_off(G) + 4 * t0);
-    r.vm[k][1] = ld_nt1(pg + vmeta_off(G) + 4 * (t0 + 2));
-  }
+  for (int T = 0; T < NT; ++T) r.vm[T] = ld_nt1(pg + vmeta_off(G) + 4 * gx_token<G>(T, j));
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const uint8_t* src = pg + vcode_off(G) + (16 * ct + j) * (G / 4) + g * (G / 16);
-    if constexpr (GqaPage<G>::VDW == 4) {
-      const uint4 t = ld_nt4(src);
-      r.vc[ct][0] = t.x; r.vc[ct][1] = t.y; r.vc[ct][2] = t.z; r.vc[ct][3] = t.w;
-    } else if constexpr (GqaPage<G>::VDW == 2) {
-      const uint2 t = ld_nt2(src);
-      r.vc[ct][0] = t.x; r.vc[ct][1] = t.y;
-    } else {
-      r.vc[ct][0] = ld_nt1(src);
+  for (int C = 0; C < 8; ++C)
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      const uint8_t* row = pg + vcode_off(G) + (16 * C + j) * (G / 4);
+      if constexpr (G >= 128) {
+        r.vc[C][h] = ld_nt2(row + 32 * h + 8 * g);
+      } else {  // a 16-byte row: lane groups 2 and 3 have no slots
+        r.vc[C][h] = ld_nt2(row + 8 * (g & 1));
+        if (g >= 2) r.vc[C][h] = make_uint2(0u, 0u);
+      }
     }
-  }
 }
 
-template <int G, int QB>
-__device__ __forceinline__ void gqa_page(const GqaPage<G>& r, int n_valid,
-                                         const float (&qs)[Geo<G, QB>::QPL][8],
-                                         GqaLds<G, QB>& L, GqaState<QB>& st, int lane) {
-  using Gm = Geo<G, QB>;
-  const int j = lane & 15, g = lane >> 4;
-  const int cg = j >> 2, cb = j & 3;
-  const uint4 &kmA = r.kmA, &kmB = r.kmB;
-  const auto& kc = r.kc;
-  const auto& vm = r.vm;
-  const auto& vc = r.vc;
+// Online softmax state of one wave for NA groups of 4 query heads; lane group
+// g holds head 4a + g of group a.
+template <int NA>
+struct GxState {
+  float m[NA];       // running max (uniform in the lane group)
+  float l[NA];       // this lane's share of the running sum
+  float vmin[NA];    // this lane's share of sum p_t min_t
+  f32x4v acc[NA][8]; // digit-row sums: channel 16C + (lane&15), rows = the head's digits
+};
 
-  // ---- q' = qs * scale_c for the lane's 8 channels (slot order); with codes
-  // entering as c/2: z = sum qs min_c + 2 sum q' c/2
+// A operand of row (lane & 15): logical k 16g..16g+15 and 64+16g..64+16g+15
+template <int G>
+__device__ __forceinline__ i32x8 gx_a(const uint8_t* blk, int lane) {
+  const uint8_t* r = blk + Gx<G>::RS * (lane & 15) + 16 * (lane >> 4);
+  const uint4 lo = *reinterpret_cast<const uint4*>(r);
+  const uint4 hi = *reinterpret_cast<const uint4*>(r + 64);
+  i32x8 a;
+  a[0] = int(lo.x); a[1] = int(lo.y); a[2] = int(lo.z); a[3] = int(lo.w);
+  a[4] = int(hi.x); a[5] = int(hi.y); a[6] = int(hi.z); a[7] = int(hi.w);
+  return a;
+}
+
+// Scale register of lane l: row l & 15 = digit (l & 3) of head (l & 15) >> 2,
+// whose exponent e lives in lane group (l & 15) >> 2; times 2 for code/2.
+__device__ __forceinline__ int gx_scale(int e, int lane) {
+  const int e0 = __builtin_amdgcn_readlane(e, 0), e1 = __builtin_amdgcn_readlane(e, 16);
+  const int e2 = __builtin_amdgcn_readlane(e, 32), e3 = __builtin_amdgcn_readlane(e, 48);
+  const int h = (lane & 15) >> 2;
+  const int eh = h == 0 ? e0 : h == 1 ? e1 : h == 2 ? e2 : e3;
+  return 124 + eh - 5 * (lane & 3);
+}
+
+// One fixed-point digit of r (r scaled so that |r| < 16 at the first digit):
+// the digit, with r left as 32 x the rest, as mx_digits does for all four.
+__device__ __forceinline__ float gx_digit(float& r) {
+  const float d = __builtin_rintf(r);
+  r = (r - d) * 32.0f;
+  return d;
+}
+
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+template <int G, int NA>
+struct alignas(16) GxLds {
+  // q' operands (NA blocks), then p' operands (NA x NB blocks); reused for the
+  // fp16 fold and the final state
+  uint8_t ab[NA * (1 + Gx<G>::NB) * Gx<G>::ABLK];
+  __device__ __forceinline__ uint8_t* qa(int a) { return ab + a * Gx<G>::ABLK; }
+  __device__ __forceinline__ uint8_t* pa(int a, int h) {
+    return ab + (NA + a * Gx<G>::NB + h) * Gx<G>::ABLK;
+  }
+  __device__ __forceinline__ float* f(int i) { return reinterpret_cast<float*>(ab) + i; }
+};
+
+template <int G, int NA>
+__device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const float (&qs)[NA][8],
+                                        GxLds<G, NA>& L, GxState<NA>& st, int lane) {
+  constexpr int NT = Gx<G>::NT, NB = Gx<G>::NB, NTB = Gx<G>::NTB, RS = Gx<G>::RS;
+  const int j = lane & 15, g = lane >> 4;
+
+  // ---- q' = qs scale_c for head g of each group, channels 8j..8j+7, as digits
   float scl[8], mnv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = kPerm(e);
-    const uint32_t w = c < 4 ? dw(kmA, c) : dw(kmB, c - 4);
-    mnv[e] = lo_f(w);
-    scl[e] = hi_f(w);
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = dw(r.km[i >> 2], i & 3);
+    mnv[i] = lo_f(w);
+    scl[i] = hi_f(w);
   }
-  float qp[Gm::QPL][8], bp[Gm::QPL];
-  float amax = 0.f;
+  // channel 8j + i sits at logical k = base + (i >> 1) + 8 (i & 1)
+  const int base = 32 * (j >> 2) + 16 * ((j >> 1) & 1) + 4 * (j & 1);
+  float bias[NA];
+  int sq[NA];
 #pragma unroll
-  for (int k = 0; k < Gm::QPL; ++k) {
-    bp[k] = 0.f;
+  for (int a = 0; a < NA; ++a) {
+    float qp[8], b = 0.f, amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qp[k][e] = qs[k][e] * scl[e];
-      bp[k] = fmaf(qs[k][e], mnv[e], bp[k]);
-      amax = fmaxf(amax, fabsf(qp[k][e]));
+    for (int i = 0; i < 8; ++i) {
+      qp[i] = qs[a][i] * scl[i];
+      b = fmaf(qs[a][i], mnv[i], b);
+      amax = fmaxf(amax, fabsf(qp[i]));
     }
-  }
-  // keep |q'| below 2^15 in fp16: scale by a power of two if the page needs it
-  const float mx = wave_max(amax);
-  const int sh = max(0, __builtin_amdgcn_frexp_expf(mx) - 15);
-  const float down = __builtin_amdgcn_ldexpf(1.0f, -sh);
-  const float zsc = __builtin_amdgcn_ldexpf(2.0f, sh);  // D -> log2 score units
+    bias[a] = row_sum(b);
+    const int eq = mx_exp(row_max(amax));
+    // digit rows one at a time (see mx_digits): r holds what is left
 #pragma unroll
-  for (int k = 0; k < Gm::QPL; ++k) {
-    const int h = g + 4 * k;
-    const float bsum = row_sum(bp[k]);
-    if (h < QB) {
-      h8 hi, lo;
+    for (int i = 0; i < 8; ++i) qp[i] = __builtin_amdgcn_ldexpf(qp[i], 4 - eq);
+    uint8_t* blk = L.qa(a);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = qp[k][e] * down;
-        const _Float16 xh = _Float16(x);
-        hi[e] = xh;
-        lo[e] = _Float16(x - float(xh));
-      }
-      *L.row(cb * 4 + cg, h) = hi;
-      *L.row((((QB + h) / 16) * 4 + cb) * 4 + cg, (QB + h) % 16) = lo;
-      if (j == 0) L.bias[h] = bsum;
+    for (int k = 0; k < 4; ++k) {
+      float d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = gx_digit(qp[i]);
+      uint8_t* row = blk + RS * (4 * g + k);
+      *reinterpret_cast<uint32_t*>(row + base) = pack4_fp8(d[0], d[2], d[4], d[6]);
+      *reinterpret_cast<uint32_t*>(row + base + 8) = pack4_fp8(d[1], d[3], d[5], d[7]);
     }
-  }
-  wave_lds_sync();
-  h8 ak[Gm::NA][4];
-#pragma unroll
-  for (int a = 0; a < Gm::NA; ++a)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ak[a][s] = *L.row((a * 4 + s) * 4 + g, j);
-
-  // ---- scores on the matrix cores, two tiles at a time into LDS
-#pragma unroll
-  for (int T = 0; T < Gm::KT; T += 2) {
-    h8 b[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      codes_b(kc[T + u].x, b[u][0], b[u][1]);
-      codes_b(kc[T + u].y, b[u][2], b[u][3]);
-    }
-    f4 d[2][Gm::NA];
-#pragma unroll
-    for (int a = 0; a < Gm::NA; ++a)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) d[u][a] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int a = 0; a < Gm::NA; ++a)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) d[u][a] = mfma16(ak[a][s], b[u][s], d[u][a]);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f4* dst = reinterpret_cast<f4*>(&L.zs[(16 * (T + u) + j) * Gm::ZR + 4 * g]);
-      if constexpr (Gm::NA == 2) {
-        *dst = d[u][0] + d[u][1];
-      } else {
-        if (4 * g < 2 * QB) *dst = d[u][0];
-      }
-    }
+    sq[a] = gx_scale(eq, lane);
   }
   wave_lds_sync();
 
-  // ---- softmax over the page: lane takes token pairs, all QB heads
-  float bias[QB];
+  // ---- scores on the matrix cores
+  float z[NA][NT];
 #pragma unroll
-  for (int h = 0; h < QB; h += 4) {
-    const float4 b4 = *reinterpret_cast<const float4*>(&L.bias[h]);
-    bias[h] = b4.x;
-    if (h + 1 < QB) bias[h + 1] = b4.y;
-    if (h + 2 < QB) bias[h + 2] = b4.z;
-    if (h + 3 < QB) bias[h + 3] = b4.w;
-  }
-  float z[Gm::PPL][2][QB];
+  for (int a = 0; a < NA; ++a) {
+    const i32x8 aq = gx_a<G>(L.qa(a), lane);
 #pragma unroll
-  for (int k = 0; k < Gm::PPL; ++k) {
-    const int pi = lane + 64 * k;
-    const bool pv = (Gm::NP % 64 == 0) || pi < Gm::NP;
-    const int t0 = pair_token<G>(min(pi, Gm::NP - 1));
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int t = t0 + 2 * s2;
-      const bool ok = pv && t < n_valid;
-      float zr[Gm::ZR];
-#pragma unroll
-      for (int i = 0; i < Gm::ZR; i += 4) {
-        const f4 v = *reinterpret_cast<const f4*>(&L.zs[t * Gm::ZR + i]);
-        zr[i] = v[0]; zr[i + 1] = v[1]; zr[i + 2] = v[2]; zr[i + 3] = v[3];
-      }
-#pragma unroll
-      for (int h = 0; h < QB; ++h) {
-        const float v = (Gm::ZR == QB) ? zr[h] : zr[h] + zr[QB + h];
-        z[k][s2][h] = ok ? fmaf(v, zsc, bias[h]) : -INFINITY;
-      }
+    for (int T = 0; T < NT; ++T) {
+      const f32x4v zr = mx_mfma<0>(aq, mx_b(r.kc[T]), f32x4v{0.f, 0.f, 0.f, 0.f}, sq[a]);
+      z[a][T] = bias[a] + ((zr[0] + zr[1]) + (zr[2] + zr[3]));
     }
   }
-  float mh[QB];
+  if (n_valid < G) {
 #pragma unroll
-  for (int h = 0; h < QB; ++h) {
-    mh[h] = -INFINITY;
+    for (int T = 0; T < NT; ++T)
+      if (gx_token<G>(T, j) >= n_valid)
 #pragma unroll
-    for (int k = 0; k < Gm::PPL; ++k) mh[h] = fmaxf(mh[h], fmaxf(z[k][0][h], z[k][1][h]));
+        for (int a = 0; a < NA; ++a) z[a][T] = -INFINITY;
   }
-  wave_max_n<QB>(mh);
-  float alpha[QB], muse[QB];
+
+  // ---- softmax: head 4a + g over the lane group's 16 lanes
   bool moved = false;
+  float alpha[NA];
 #pragma unroll
-  for (int h = 0; h < QB; ++h) {
-    const float mn = fmaxf(st.m[h], mh[h]);
-    alpha[h] = (mn == st.m[h]) ? 1.f : (st.m[h] == -INFINITY ? 0.f : exp2_fast(st.m[h] - mn));
-    moved |= (mn != st.m[h]);
-    st.m[h] = mn;
-    muse[h] = (mn == -INFINITY) ? 0.f : mn;
-    st.l[h] *= alpha[h];
-    st.vmin[h] *= alpha[h];
+  for (int a = 0; a < NA; ++a) {
+    float mx = z[a][0];
+#pragma unroll
+    for (int T = 1; T < NT; ++T) mx = fmaxf(mx, z[a][T]);
+    mx = row_max(mx);
+    const float mn = fmaxf(st.m[a], mx);
+    alpha[a] = (mn == st.m[a]) ? 1.f : (st.m[a] == -INFINITY ? 0.f : exp2_fast(st.m[a] - mn));
+    moved |= (mn != st.m[a]);
+    st.m[a] = mn;
+    st.l[a] *= alpha[a];
+    st.vmin[a] *= alpha[a];
   }
-  if (moved) {  // wave-uniform
-    float ar[4];
+  if (__ballot(moved) != 0) {  // wave-uniform
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ar[r] = row_pick<QB>(alpha, g, r);
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.acc[ct][r] *= ar[r];
+      for (int C = 0; C < 8; ++C) st.acc[a][C] *= alpha[a];
   }
+  int sp[NA];
 #pragma unroll
-  for (int k = 0; k < Gm::PPL; ++k) {
-    const int pi = lane + 64 * k;
-    const bool pv = (Gm::NP % 64 == 0) || pi < Gm::NP;
-    const int g2 = pi / (G / 8), rem = pi % (G / 8), kb = rem >> 2, p = rem & 3;
-    float pp[2][QB];
+  for (int a = 0; a < NA; ++a) {
+    // a page without members leaves m at -inf only if nothing came before;
+    // its weights are then 0 (m = -inf -> use 0 as the reference)
+    const float mref = (st.m[a] == -INFINITY) ? 0.f : st.m[a];
+    float pp[NT], pmax = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const float mnt = lo_f(vm[k][s2]), sct = hi_f(vm[k][s2]);
+    for (int T = 0; T < NT; ++T) {
+      const float p = exp2_fast(z[a][T] - mref);
+      st.l[a] += p;
+      st.vmin[a] = fmaf(p, lo_f(r.vm[T]), st.vmin[a]);
+      pp[T] = p * hi_f(r.vm[T]);
+      pmax = fmaxf(pmax, pp[T]);
+    }
+    const int ep = mx_exp(row_max(pmax));
 #pragma unroll
-      for (int h = 0; h < QB; ++h) {
-        const float pr = exp2_fast(z[k][s2][h] - muse[h]);
-        st.l[h] += pr;
-        st.vmin[h] = fmaf(pr, mnt, st.vmin[h]);
-        pp[s2][h] = pr * sct;  // p * scale_t <= 2^16 / 3 fits fp16
+    for (int T = 0; T < NT; ++T) pp[T] = __builtin_amdgcn_ldexpf(pp[T], 4 - ep);
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      uint8_t* blk = L.pa(a, h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float d[NTB];
+#pragma unroll
+        for (int t = 0; t < NTB; ++t) d[t] = gx_digit(pp[h * NTB + t]);
+        uint8_t* dst = blk + RS * (4 * g + k) + NTB * j;
+        if constexpr (NTB == 8) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack4_fp8(d[0], d[1], d[2], d[3]),
+                                                      pack4_fp8(d[4], d[5], d[6], d[7]));
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = pack4_fp8(d[0], d[1], d[2], d[3]);
+        }
       }
     }
-    uint32_t* prow = reinterpret_cast<uint32_t*>(L.ab + (kb * 4 + g2) * Gm::kBlk) + p;
-#pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      const f16x2 two{_Float16(pp[0][h]), _Float16(pp[1][h])};
-      if (pv) prow[4 * h] = __builtin_bit_cast(uint32_t, two);
-    }
+    sp[a] = gx_scale(ep, lane);
   }
   wave_lds_sync();
 
   // ---- values on the matrix cores
-  h8 av[Gm::KB];
 #pragma unroll
-  for (int kb = 0; kb < Gm::KB; ++kb) av[kb] = *L.row(kb * 4 + g, j);
+  for (int a = 0; a < NA; ++a) {
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
+    for (int h = 0; h < NB; ++h) {
+      i32x8 ap = gx_a<G>(L.pa(a, h), lane);
+      if constexpr (G < 128) {  // logical k >= 64 has no slots (and no written bytes)
+        ap[4] = 0; ap[5] = 0; ap[6] = 0; ap[7] = 0;
+      }
 #pragma unroll
-    for (int w = 0; w < Gm::VDW; ++w) {
-      h8 b0, b1;
-      codes_b(vc[ct][w], b0, b1);
-      st.acc[ct] = mfma16(av[2 * w], b0, st.acc[ct]);
-      st.acc[ct] = mfma16(av[2 * w + 1], b1, st.acc[ct]);
+      for (int C = 0; C < 8; ++C) st.acc[a][C] = mx_mfma<0>(ap, mx_b(r.vc[C][h]), st.acc[a][C], sp[a]);
     }
   }
   wave_lds_sync();
 }
 
-// Work-group = 4 waves on one (sequence, KV head, split). Every wave holds the
-// state of QB query heads, walks the split's fp16 tokens (its 16-token chunks,
-// one head at a time) and then its pages (round-robin); the 4 states merge in
-// LDS. More than QB heads per KV head run as several passes.
-template <int G, int QB>
-__global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ? 3 : 2) void decode_gqa_kernel(Arena a, const __half* __restrict__ q,
-                                                         __half* __restrict__ out, int S,
-                                                         HeadOrder order) {
-  using Gm = Geo<G, QB>;
-  __shared__ GqaLds<G, QB> lds_all[kWaves];
+// Work-group = 4 waves on one (sequence, KV head, split). Each pass serves
+// 4 NA query heads of the KV head: every wave walks its share of the split's
+// fp16 tokens (16-token chunks, one load per group of 4 heads), folds them into
+// its state, then walks its pages (round-robin); the 4 wave states merge in
+// LDS. Heads past the KV head's last (a padded group) get a zero query and are
+// not written.
+template <int G, int NA>
+__global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_gqa_kernel(
+    Arena a, const __half* __restrict__ q, __half* __restrict__ out, int S, HeadOrder order) {
+  constexpr int QB = 4 * NA;
+  __shared__ GxLds<G, NA> lds_all[kWaves];
   __shared__ float mg_m[kWaves][QB], mg_l[kWaves][QB];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
-  GqaLds<G, QB>& L = lds_all[wave];
+  GxLds<G, NA>& L = lds_all[wave];
   const int NQ = a.Hq / a.Hkv;
   const int s = blockIdx.x % S;
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);
@@ -418,26 +315,28 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
   for (int q0 = 0; q0 < NQ; q0 += QB) {
     const int qh0 = hk * NQ + q0;
     const __half* qbase = q + (size_t(b) * a.Hq + qh0) * D;
-    GqaState<QB> st;
+    GxState<NA> st;
 #pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      st.m[h] = -INFINITY;
-      st.l[h] = 0.f;
-      st.vmin[h] = 0.f;
+    for (int x = 0; x < NA; ++x) {
+      st.m[x] = -INFINITY;
+      st.l[x] = 0.f;
+      st.vmin[x] = 0.f;
+#pragma unroll
+      for (int C = 0; C < 8; ++C) st.acc[x][C] = f32x4v{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // fp16 tokens: each chunk is loaded once per group of up to 4 heads; the
-    // heads' states then enter the page state (which is still empty)
-    constexpr int HG = QB < 4 ? QB : 4;
-#pragma unroll 1
-    for (int h0 = 0; h0 < QB; h0 += HG) {
-      uint4 q8[HG];
-      Fp16State fs[HG];
+    // fp16 tokens: each chunk is loaded once per group of 4 heads; the heads'
+    // states then become the (still empty) page states, the accumulator in
+    // digit row 0
 #pragma unroll
-      for (int i = 0; i < HG; ++i) {
-        q8[i] = reinterpret_cast<const uint4*>(qbase + size_t(h0 + i) * D)[lane & 15];
+    for (int x = 0; x < NA; ++x) {
+      uint4 q8[4];
+      Fp16State fs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = q0 + 4 * x + i < NQ;
+        q8[i] = live ? reinterpret_cast<const uint4*>(qbase + size_t(4 * x + i) * D)[lane & 15]
+                     : make_uint4(0u, 0u, 0u, 0u);
         fs[i].m = -INFINITY;
         fs[i].l = 0.f;
 #pragma unroll
@@ -448,85 +347,81 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
         Fp16Rows rows;
         fp16_load(src, ch, cnt, rows, lane);
 #pragma unroll
-        for (int i = 0; i < HG; ++i) fp16_attend(rows, cnt, q8[i], qscale, fs[i], lane);
+        for (int i = 0; i < 4; ++i) fp16_attend(rows, cnt, q8[i], qscale, fs[i], lane);
       }
 #pragma unroll
-      for (int i = 0; i < HG; ++i) {
-        const int h = h0 + i;
+      for (int i = 0; i < 4; ++i) {
+        const float lt = wave_sum(fs[i].l);
+        float v[8];
 #pragma unroll
-        for (int hh = 0; hh < QB; ++hh) {
-          if (hh == h) {
-            st.m[hh] = fs[i].m;
-            st.l[hh] = fs[i].l;
-          }
+        for (int e = 0; e < 8; ++e) {  // the four token rows of each channel add up
+          f32x2 p = swap16(fs[i].acc[e]);
+          const float y = p.x + p.y;
+          p = swap32(y);
+          v[e] = p.x + p.y;
         }
-        float4* f = reinterpret_cast<float4*>(&L.zs[(lane >> 4) * D + 8 * (lane & 15)]);
-        f[0] = make_float4(fs[i].acc[0], fs[i].acc[1], fs[i].acc[2], fs[i].acc[3]);
-        f[1] = make_float4(fs[i].acc[4], fs[i].acc[5], fs[i].acc[6], fs[i].acc[7]);
+        float* f = L.f(0);
+        if (lane < 16) {
+          reinterpret_cast<float4*>(f + 8 * lane)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(f + 8 * lane)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
         wave_lds_sync();
+        if (g == i) {
+          st.m[x] = fs[i].m;
+          st.l[x] = (j == 0) ? lt : 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const int c = 16 * ct + j;
-          const float v = (L.zs[c] + L.zs[D + c] + L.zs[2 * D + c] + L.zs[3 * D + c]) * 0.5f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * g + r == h) st.acc[ct][r] = v;
+          for (int C = 0; C < 8; ++C) st.acc[x][C][0] = f[16 * C + j];
         }
         wave_lds_sync();
       }
     }
 
-    // the lane's query values for the q' step: heads g + 4k, channels
-    // 8j + kPerm(slot)
-    float qs[Gm::QPL][8];
+    // the lane's query values for the q' step: head 4x + g, channels 8j..8j+7
+    float qs[NA][8];
 #pragma unroll
-    for (int k = 0; k < Gm::QPL; ++k) {
-      const int h = g + 4 * k;
-      if (h < QB) {
-        const uint4 q8 = *reinterpret_cast<const uint4*>(qbase + size_t(h) * D + 8 * j);
+    for (int x = 0; x < NA; ++x) {
+      if (q0 + 4 * x + g < NQ) {
+        const uint4 q8 = *reinterpret_cast<const uint4*>(qbase + size_t(4 * x + g) * D + 8 * j);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = kPerm(e);
-          const uint32_t w = dw(q8, c >> 1);
-          qs[k][e] = ((c & 1) ? hi_f(w) : lo_f(w)) * qscale;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = dw(q8, i >> 1);
+          qs[x][i] = ((i & 1) ? hi_f(w) : lo_f(w)) * qscale;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qs[k][e] = 0.f;
+        for (int i = 0; i < 8; ++i) qs[x][i] = 0.f;
       }
     }
 
     // pages, each wave every 4th
     for (int u = sp.p0 + wave; u < sp.p1; u += kWaves) {
       prio_by_work_left((sp.p1 - u + kWaves - 1) / kWaves);
-      GqaPage<G> pr;
-      gqa_load<G>(pr, pages + size_t(u) * PB, lane);
-      gqa_page<G, QB>(pr, page_nvalid(a.G, a.P, u), qs, L, st, lane);
+      GxPage<G> pr;
+      gx_load<G>(pr, pages + size_t(u) * PB, lane);
+      gx_page<G, NA>(pr, page_nvalid(a.G, a.P, u), qs, L, st, lane);
     }
 
-    // this wave's state -> LDS: fin[h][c] = sum p' c + sum p min = 2 acc + vmin
-    float vt[QB];
+    // this wave's state -> LDS: fin[h][c] = sum of the digit rows + sum p min
+    float* fin = L.f(0);
 #pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      const float lt = wave_sum(st.l[h]);
-      vt[h] = wave_sum(st.vmin[h]);
-      if (lane == 0) {
-        mg_m[wave][h] = st.m[h];
+    for (int x = 0; x < NA; ++x) {
+      const float lt = row_sum(st.l[x]);
+      const float vt = row_sum(st.vmin[x]);
+      const int h = 4 * x + g;
+      if (j == 0) {
+        mg_m[wave][h] = st.m[x];
         mg_l[wave][h] = lt;
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      const float v = row_pick<QB>(vt, g, r);
-      if (h < QB) {
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) L.zs[h * D + 16 * ct + j] = fmaf(st.acc[ct][r], 2.0f, v);
+      for (int C = 0; C < 8; ++C) {
+        const f32x4v v = st.acc[x][C];
+        fin[h * D + 16 * C + j] = ((v[0] + v[1]) + (v[2] + v[3])) + vt;
       }
     }
     __syncthreads();
     for (int x = threadIdx.x; x < QB * D; x += blockDim.x) {
       const int h = x / D, c = x % D;
+      if (q0 + h >= NQ) continue;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mg_m[w][h]);
@@ -535,7 +430,7 @@ __global__ __launch_bounds__(256, (G * QB >= 2048) ? 1 : (G <= 128 && QB <= 4) ?
       for (int w = 0; w < kWaves; ++w) {
         const float f = (mg_m[w][h] == -INFINITY) ? 0.f : exp2f(mg_m[w][h] - M);
         Ls = fmaf(mg_l[w][h], f, Ls);
-        A = fmaf(lds_all[w].zs[h * D + c], f, A);
+        A = fmaf(lds_all[w].f(0)[h * D + c], f, A);
       }
       const int qh = qh0 + h;
       if (S == 1) {
@@ -558,16 +453,10 @@ hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, const H
                     hipStream_t s) {
   const int NQ = a.Hq / a.Hkv;
   const dim3 grid(unsigned(a.B) * a.Hkv * S), block(64 * kWaves);
-  if (NQ % 16 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 16>), grid, block, 0, s, a, q, out, S, order);
-  } else if (NQ % 8 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 8>), grid, block, 0, s, a, q, out, S, order);
-  } else if (NQ % 4 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 4>), grid, block, 0, s, a, q, out, S, order);
-  } else if (NQ == 2) {
+  if (NQ % 8 == 0) {
     hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S, order);
   } else {
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 1>), grid, block, 0, s, a, q, out, S, order);
   }
   return hipGetLastError();
 }
@@ -576,12 +465,10 @@ template <int G>
 int wgs_g(const Arena& a) {
   const int NQ = a.Hq / a.Hkv;
   int n = 0;
-  hipError_t e = hipErrorInvalidValue;
   const int bs = 64 * kWaves;
-  if (NQ % 16 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 16>, bs, 0);
-  else if (NQ % 8 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 8>, bs, 0);
-  else if (NQ % 4 == 0) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 4>, bs, 0);
-  else if (NQ == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 2>, bs, 0);
+  const hipError_t e =
+      (NQ % 8 == 0) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 2>, bs, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 1>, bs, 0);
   return e == hipSuccess ? n : 0;
 }
 

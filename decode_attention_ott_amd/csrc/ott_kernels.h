@@ -1,6 +1,7 @@
 // Internal interface between the host library (ott_api.cpp) and the HIP kernels.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +51,13 @@ struct QuantizeList {
   uint16_t b[kMaxBatch];
 };
 hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s);
+// Prompt lengths of an ott_prefill call.
+struct PrefillLens {
+  int32_t len[kMaxBatch];
+};
+// k, v: fp16 [B][Hkv][max_len][D]; the cache must be empty.
+hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
+                          const PrefillLens& lens, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
                          const HeadOrder& order, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it
@@ -60,6 +68,25 @@ hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int num_s
 // one CU at once (0 if the runtime cannot tell).
 int decode_wgs_per_cu(const Arena& a);
 int decode_gqa_wgs_per_cu(const Arena& a);
+
+// The fp16 baseline decode: a plain fp16 KV cache [B][Hkv][max_len][D] and one
+// query per (sequence, query head); part holds [B][Hq][S][2+D] split partials.
+struct Fp16Cache {
+  const __half* k;
+  const __half* v;
+  const __half* q;
+  __half* out;
+  float* part;
+  int32_t B, Hq, Hkv, max_len;
+  float sm_scale;
+};
+struct Fp16Lens {
+  int32_t len[kMaxBatch];
+};
+int fp16_heads_per_pass(int nq);
+int fp16_decode_wgs_per_cu(int nq);
+hipError_t launch_fp16_decode(const Fp16Cache& c, const Fp16Lens& lens, int num_splits,
+                              hipStream_t s);
 
 // Dynamic LDS bytes the quantize kernel needs for (G, P).
 size_t quantize_lds_bytes(int G, int P);

@@ -54,7 +54,7 @@ typedef enum {
 /* Layer shape and OTT hyper-parameters ([Blog] 3.1-3.3, section 4 and 6). */
 typedef struct {
   int32_t batch;        /* B, 1..512 */
-  int32_t num_q_heads;  /* Hq, a multiple of Hkv; Hq/Hkv must be 1, 2 or a multiple of 4 */
+  int32_t num_q_heads;  /* Hq, a multiple of Hkv with Hq/Hkv <= 64 */
   int32_t num_kv_heads; /* Hkv >= 1 */
   int32_t head_dim;     /* d, must be 128 */
   int32_t group_size;   /* G: tokens per quantized group, 64, 128 or 256 */
@@ -180,6 +180,33 @@ ott_status_t ott_get_seq_state(ott_handle_t h, int32_t b, int32_t out[4]);
  * 1..max_splits work-groups per (sequence, KV head). Results agree to rounding.
  */
 ott_status_t ott_set_num_splits(ott_handle_t h, int32_t num_splits);
+
+/*
+ * ott_fp16_decode - the comparison point of the pages' throughput figure
+ * ([Abs] Figure 3(a); [Blog] section 4: OTT decodes 2.3x faster than the model
+ * on its ordinary FP16 KV cache at batch 32): single-query decode attention over
+ * an uncompressed fp16 KV cache, no quantization, no pool, no window.
+ * For each sequence b and query head qh (KV head qh / (Hq/Hkv)):
+ *   out[b][qh] = sum_t softmax_t(sm_scale * q[b][qh] . k[b][kvh][t]) v[b][kvh][t],
+ *   t = 0..h_len[b]-1.
+ *   d_k, d_v   : device fp16 [batch][num_kv_heads][max_len][head_dim], 16-byte aligned;
+ *                rows at and past h_len[b] are not read.
+ *   h_len      : host int32 [batch], 1 <= h_len[b] <= max_len (else OTT_ERR_STATE).
+ *   d_q, d_out : device fp16 [batch][num_q_heads][head_dim], 16-byte aligned.
+ *   sm_scale   : <= 0 selects 1/sqrt(head_dim). head_dim must be 128 (else OTT_ERR_UNSUPPORTED).
+ *   d_work     : caller-owned device workspace for split partials (may be NULL, then one
+ *                split); work_bytes its size. num_splits: 0 = automatic (fits the workspace),
+ *                1 = no workspace used, n > 1 needs ott_fp16_decode_workspace(batch, Hq, n)
+ *                bytes (else OTT_ERR_ARENA_TOO_SMALL, nothing enqueued).
+ * Stateless: no handle, no allocation, no synchronization. A failed launch returns
+ * OTT_ERR_HIP.
+ */
+ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, const void* d_k, const void* d_v, int32_t max_len,
+                             const int32_t* h_len, const void* d_q, void* d_out, float sm_scale,
+                             void* d_work, size_t work_bytes, int32_t num_splits, void* stream);
+/* ott_fp16_decode_workspace - bytes of d_work that num_splits splits need (0 for <= 1). */
+size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits);
 
 /* ott_status_string - static text for a status code. */
 const char* ott_status_string(ott_status_t s);

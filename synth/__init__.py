@@ -38,6 +38,7 @@ _TAG_K = 3
 _TAG_V = 4
 _TAG_TOK = 5
 _TAG_Q = 6
+_TAG_SIGN = 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -59,6 +60,7 @@ class Workload:
     tok_prob: float = 0.005
     tok_scale: float = 0.05
     n_outlier_channels: int = 4
+    one_signed: bool = False
 
     @property
     def max_prefill(self) -> int:
@@ -109,6 +111,9 @@ def kv_stream(w: Workload, b: int, kvh: int, n_pos: int) -> Tuple[np.ndarray, np
     tok = _rng(w.seed, _TAG_TOK, b, kvh).random(n_pos) < w.tok_prob
     ch = outlier_channels(w, kvh)
     if ch.size:
+        if w.one_signed:
+            sign = np.where(_rng(w.seed, _TAG_SIGN, kvh).random(ch.size) < 0.5, -1.0, 1.0)
+            k[:, ch] = np.abs(k[:, ch]) * sign.astype(np.float32)
         k[:, ch] *= np.float32(w.chan_scale)
         k[np.ix_(tok, ch)] *= np.float32(w.tok_scale)
     return k.astype(np.float16), v.astype(np.float16)

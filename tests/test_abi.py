@@ -57,9 +57,15 @@ def test_sizing_matches_layout_formula():
     assert req == want
 
 
+def test_any_head_ratio_up_to_64_is_accepted():
+    for hq, hkv in [(6, 2), (10, 2), (128, 2), (7, 7)]:
+        st, _ = _sizing(_cfg(num_q_heads=hq, num_kv_heads=hkv))
+        assert st == 0, (hq, hkv)
+
+
 @pytest.mark.parametrize("bad,status", [
     (dict(head_dim=64), 2), (dict(group_size=96), 2), (dict(group_size=32), 2),
-    (dict(num_q_heads=3), 1), (dict(num_q_heads=6, num_kv_heads=2), 2),
+    (dict(num_q_heads=3), 1), (dict(num_q_heads=130, num_kv_heads=2), 2),
     (dict(batch=0), 1), (dict(batch=513), 2), (dict(pool_size=-1), 1), (dict(pool_size=600), 2),
     (dict(residual=-1), 1), (dict(max_seq_len=0), 1), (dict(sm_scale=float("nan")), 1),
 ])
@@ -87,3 +93,29 @@ def test_calls_validate_before_any_gpu_work():
     assert lib.ott_set_num_splits(None, 1) == 1
     lib.ott_destroy(None)
     assert L.ott_status_string(4) == "window or sequence capacity exceeded"
+
+
+def test_fp16_baseline_validates_before_any_gpu_work():
+    from decode_attention_ott_amd import _lib as L
+    lib = L.lib
+    ln = (ctypes.c_int32 * 2)(10, 10)
+    P = ctypes.c_void_p(4096)
+    args = dict(batch=2, hq=4, hkv=2, d=128, k=P, v=P, max_len=16, ln=ln, q=P, out=P, sm=0.0,
+                work=None, wb=0, s=1, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.ott_fp16_decode(a["batch"], a["hq"], a["hkv"], a["d"], a["k"], a["v"],
+                                   a["max_len"], a["ln"], a["q"], a["out"], a["sm"], a["work"],
+                                   a["wb"], a["s"], a["st"])
+    assert call(batch=0) == 1
+    assert call(hq=3) == 1                       # not a multiple of the KV heads
+    assert call(d=64) == 2                       # head_dim must be 128
+    assert call(k=None) == 1
+    assert call(q=ctypes.c_void_p(4096 + 8)) == 1  # misaligned
+    assert call(ln=(ctypes.c_int32 * 2)(10, 17)) == 5  # a length above max_len
+    assert call(ln=(ctypes.c_int32 * 2)(0, 3)) == 5    # an empty sequence
+    assert call(s=4) == 3                        # splits without a workspace
+    assert call(s=-1) == 1
+    assert L.ott_fp16_decode_workspace(2, 4, 1) == 0
+    assert L.ott_fp16_decode_workspace(2, 4, 3) == 2 * 4 * 3 * 130 * 4

@@ -45,8 +45,10 @@ def test_parameters(G, R, P, L, steps):
              state_every_step=True)
 
 
-# query-head groups of 2, 4, 8, 16 and 32 (two passes of 16) per KV head
-@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (16, 2), (12, 3), (32, 2), (64, 2)])
+# query heads per KV head: 2 and 3 (a padded group of 4), 4, 6 (a group and a
+# padded one), 8 (two groups), 16 and 32 (passes of 8)
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 2), (8, 2), (12, 2), (16, 2), (12, 3), (32, 2),
+                                    (64, 2)])
 def test_grouped_query_heads(Hq, Hkv):
     run_case(small(f"gqa{Hq}x{Hkv}", Hq=Hq, Hkv=Hkv, L=(520, 520), steps=6, seed=Hq))
 
