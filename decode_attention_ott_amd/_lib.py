@@ -23,7 +23,7 @@ STATUS_NAMES = {
 # Every symbol include/ott.h declares.
 EXPORTS = ("ott_init", "ott_append", "ott_quantize_group", "ott_decode", "ott_destroy",
            "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits", "ott_status_string",
-           "ott_fp16_decode", "ott_fp16_decode_workspace")
+           "ott_fp16_decode", "ott_fp16_decode_workspace", "ott_prefill")
 
 
 class ott_config_t(ctypes.Structure):
@@ -72,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.ott_get_seq_state.restype = ctypes.c_int
     lib.ott_set_num_splits.argtypes = [H, I32]
     lib.ott_set_num_splits.restype = ctypes.c_int
+    lib.ott_prefill.argtypes = [H, VP, VP, P(I32), I32, VP]
+    lib.ott_prefill.restype = ctypes.c_int
     lib.ott_fp16_decode.argtypes = [I32, I32, I32, I32, VP, VP, I32, P(I32), VP, VP, ctypes.c_float,
                                     VP, ctypes.c_size_t, I32, VP]
     lib.ott_fp16_decode.restype = ctypes.c_int
@@ -123,6 +125,12 @@ def ott_quantize_group(h, stream: int) -> int:
     _check(lib.ott_quantize_group(h, ctypes.c_void_p(stream), ctypes.byref(n)),
            "ott_quantize_group")
     return int(n.value)
+
+
+def ott_prefill(h, d_k: int, d_v: int, lens, max_len: int, stream: int) -> None:
+    arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+    _check(lib.ott_prefill(h, ctypes.c_void_p(d_k), ctypes.c_void_p(d_v), arr, max_len,
+                           ctypes.c_void_p(stream)), "ott_prefill")
 
 
 def ott_decode(h, d_q: int, d_out: int, stream: int) -> None:

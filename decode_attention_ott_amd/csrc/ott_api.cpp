@@ -241,6 +241,38 @@ ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_qua
   return OTT_OK;
 }
 
+ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const int32_t* h_len,
+                         int32_t max_len, void* stream) {
+  ott_status_t st = check_handle(h);
+  if (st != OTT_OK) return st;
+  if (!h_len || max_len < 0) return OTT_ERR_INVALID_ARG;
+  const int B = h->cfg.batch, G = h->cfg.group_size, R = h->cfg.residual, C = h->dev.C;
+  ott::PrefillLens lens;
+  bool any = false;
+  for (int b = 0; b < B; ++b) {
+    if (h->L[b] != 0) return OTT_ERR_STATE;  // prefill starts from an empty cache
+    if (h_len[b] < 0 || h_len[b] > max_len) return OTT_ERR_INVALID_ARG;
+    if (h_len[b] > h->cfg.max_seq_len) return OTT_ERR_CAPACITY;
+    lens.len[b] = h_len[b];
+    any |= h_len[b] > 0;
+  }
+  if (!any) return OTT_OK;
+  if (!d_k || !d_v || (reinterpret_cast<uintptr_t>(d_k) & 15) || (reinterpret_cast<uintptr_t>(d_v) & 15))
+    return OTT_ERR_INVALID_ARG;
+  st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens,
+                                           static_cast<hipStream_t>(stream)));
+  if (st != OTT_OK) return st;
+  for (int b = 0; b < B; ++b) {
+    const int L = h_len[b];
+    const int nq = L >= R + G ? (L - R) / G : 0;
+    h->L[b] = L;
+    h->rcnt[b] = L - G * nq;
+    h->head[b] = (G * nq) % C;
+    h->nb[b] = nq;
+  }
+  return OTT_OK;
+}
+
 ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream) {
   ott_status_t st = check_handle(h);
   if (st != OTT_OK) return st;

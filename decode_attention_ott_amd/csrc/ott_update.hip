@@ -7,6 +7,7 @@
 //   append_kernel    fp16 window update ([Blog] 3.3, residual window)
 //   quantize_kernel  quantization stage: Key norms, pool competition, 2-bit
 //                    pages ([Blog] 3.1, 3.2, flowchart; [Abs] Fig. 2 bottom)
+//   prefill_kernel   a whole prompt through the same steps, in order, in one launch
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -123,14 +124,15 @@ __device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, R
   }
 }
 
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, QuantizeList due) {
-  extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int h = blockIdx.x, b = due.b[blockIdx.y];
-  const int bh = b * a.Hkv + h;
-  const int G = a.G, P = a.P, C = a.C;
-  int32_t* ctr = counters(a, bh);
-  const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
-  if (r_cnt < C) return;  // window not full: nothing to do for this sequence
+// One quantize step of (sequence, KV head) bh: the group's G tokens are rows
+// (g_head + j) % g_mod of gk/gv (the window ring, or a prompt), competing with
+// the pool of buffer nb & 1; writes page nb, the new pool into the other
+// buffer and the page's member list. Counters are the caller's.
+__device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
+                                              const __half* __restrict__ gk,
+                                              const __half* __restrict__ gv, int g_head,
+                                              int g_mod, uint8_t* lds_raw) {
+  const int G = a.G, P = a.P;
   const int tid = threadIdx.x;
   const int pc = min(P, G * nb);  // pool tokens before this step
   const int NC = pc + G;          // candidates: pool + group
@@ -141,13 +143,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
 
   const __half* pk = pool_k(a, cur, bh);
   const __half* pv = pool_v(a, cur, bh);
-  const __half* rk = ring_k(a, bh);
-  const __half* rv = ring_v(a, bh);
   auto krow = [&](int src) -> const __half* {
-    return (src & kRingFlag) ? rk + size_t(src & ~kRingFlag) * D : pk + size_t(src) * D;
+    return (src & kRingFlag) ? gk + size_t(src & ~kRingFlag) * D : pk + size_t(src) * D;
   };
   auto vrow = [&](int src) -> const __half* {
-    return (src & kRingFlag) ? rv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
+    return (src & kRingFlag) ? gv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
   };
 
   // 1. candidates; squared Key norms of the group, fp64 in channel order
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
       s.src[i] = i;
     } else {
       const int j = i - pc;
-      const int slot = (head + j) % C;
-      const uint4* row = reinterpret_cast<const uint4*>(rk + size_t(slot) * D);
+      const int slot = (g_head + j) % g_mod;
+      const uint4* row = reinterpret_cast<const uint4*>(gk + size_t(slot) * D);
       uint4 w[D / 8];
 #pragma unroll
       for (int c8 = 0; c8 < D / 8; ++c8) w[c8] = row[c8];
@@ -370,10 +370,64 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
   if (tid == 0)
     reinterpret_cast<int32_t*>(a.base + a.off_page_nvalid)[size_t(bh) * a.nb_max + nb] = n_valid;
   __syncthreads();
-  if (tid == 0) {
-    ctr[1] = r_cnt - G;
-    ctr[2] = (head + G) % C;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, QuantizeList due) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const int h = blockIdx.x, b = due.b[blockIdx.y];
+  const int bh = b * a.Hkv + h;
+  int32_t* ctr = counters(a, bh);
+  const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
+  if (r_cnt < a.C) return;  // window not full: nothing to do for this sequence
+  quantize_step(a, bh, nb, ring_k(a, bh), ring_v(a, bh), head, a.C, lds_raw);
+  if (threadIdx.x == 0) {
+    ctr[1] = r_cnt - a.G;
+    ctr[2] = (head + a.G) % a.C;
     ctr[3] = nb + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill: a prompt of L_b tokens per sequence into an empty cache, with the
+// same result as appending it and running every due quantize step in order.
+// A window is full at R+G tokens and a step removes G, so the prompt makes
+// nq = floor((L - R) / G) pages (0 when L < R + G): one work-group per
+// (sequence, KV head) runs the steps in position order (each step's pool is
+// the previous step's), then the last L - G nq tokens form the window, whose
+// head slot is where G nq single steps would have left it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kQuantThreads) void prefill_kernel(Arena a,
+                                                                const __half* __restrict__ k,
+                                                                const __half* __restrict__ v,
+                                                                int64_t max_len, PrefillLens lens) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int bh = b * a.Hkv + h;
+  const int L = lens.len[b];
+  if (L == 0) return;
+  const int G = a.G, C = a.C;
+  const int nq = L >= a.R + G ? (L - a.R) / G : 0;
+  const __half* kb = k + size_t(bh) * max_len * D;
+  const __half* vb = v + size_t(bh) * max_len * D;
+  for (int n = 0; n < nq; ++n)
+    quantize_step(a, bh, n, kb + size_t(n) * G * D, vb + size_t(n) * G * D, 0, G, lds_raw);
+  const int rc = L - G * nq, head = (G * nq) % C;
+  uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
+  uint4* rv = reinterpret_cast<uint4*>(ring_v(a, bh));
+  const uint4* sk = reinterpret_cast<const uint4*>(kb + size_t(G) * nq * D);
+  const uint4* sv = reinterpret_cast<const uint4*>(vb + size_t(G) * nq * D);
+  for (int i = threadIdx.x; i < rc * (D / 8); i += blockDim.x) {
+    const int t = i / (D / 8), c = i % (D / 8);
+    const int slot = (head + t) % C;
+    rk[size_t(slot) * (D / 8) + c] = sk[i];
+    rv[size_t(slot) * (D / 8) + c] = sv[i];
+  }
+  if (threadIdx.x == 0) {
+    int32_t* ctr = counters(a, bh);
+    ctr[0] = L;
+    ctr[1] = rc;
+    ctr[2] = head;
+    ctr[3] = nq;
   }
 }
 
@@ -393,6 +447,19 @@ size_t quantize_lds_bytes(int G, int P) {
   return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
          2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
          G * sizeof(int);
+}
+
+hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
+                          const PrefillLens& lens, hipStream_t s) {
+  const size_t lds = quantize_lds_bytes(a.G, a.P);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(prefill_kernel, dim3(a.Hkv, a.B), dim3(kQuantThreads), lds, s, a,
+                     static_cast<const __half*>(k), static_cast<const __half*>(v), max_len, lens);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s) {

@@ -103,6 +103,20 @@ class OTTLayer:
             raise ValueError("k and v shapes differ")
 
     def prefill(self, K: torch.Tensor, V: torch.Tensor, lengths: Sequence[int]) -> None:
+        """Tokens [0, lengths[b]) of K, V (fp16 [B, Hkv, >=max(lengths), d] on the
+        device) into the cache. An empty cache takes the whole prompt in one
+        ott_prefill call; otherwise the tokens go through prefill_stepwise."""
+        lengths = [int(x) for x in lengths]
+        if all(self.seq_state(b)[0] == 0 for b in range(self.B)):
+            self._check_kv(K, V)
+            if max(lengths) > K.shape[2]:
+                raise ValueError("lengths exceed the rows of K and V")
+            L.ott_prefill(self.handle, K.data_ptr(), V.data_ptr(), lengths, K.shape[2],
+                          _stream())
+            return
+        self.prefill_stepwise(K, V, lengths)
+
+    def prefill_stepwise(self, K: torch.Tensor, V: torch.Tensor, lengths: Sequence[int]) -> None:
         """Appends tokens [0, lengths[b]) of K, V (fp16 [B, Hkv, >=max(lengths), d] on
         the device) in chunks that fit the window, quantizing whenever a window
         is full: the ordinary append/quantize sequence, in position order."""

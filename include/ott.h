@@ -151,6 +151,22 @@ ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const 
 ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_quantized);
 
 /*
+ * ott_prefill - a whole prompt into an empty cache in one call, with exactly the
+ * state that appending it token by token and running every due quantize step in
+ * order would leave ([Blog] 3.1: the quantization stage runs every G tokens; the
+ * prompt is processed group by group in position order, each group competing with
+ * the pool the previous groups left). Sequence b gets floor((len - R) / G) pages
+ * (0 when len < R + G) and its last len - G*pages tokens in the window.
+ *   d_k, d_v : device fp16 [B][Hkv][max_len][d], 16-byte aligned; token i of
+ *              sequence b is row i (position i).
+ *   h_len    : host int32 [B], 0 <= h_len[b] <= max_len (else OTT_ERR_INVALID_ARG),
+ *              h_len[b] <= max_seq_len (else OTT_ERR_CAPACITY).
+ *   Every sequence must be empty (else OTT_ERR_STATE, nothing enqueued). One launch,
+ *   one work-group per (sequence, KV head); a no-op when every length is 0.
+ */
+ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const int32_t* h_len,
+                         int32_t max_len, void* stream);
+/*
  * ott_decode - the decoding stage ([Blog] flowchart and 3.3; [Abs] Figure 2 top).
  * For each sequence b and query head qh (KV head qh / (Hq/Hkv)):
  *   out = sum_i softmax_i(sm_scale * q.k_i) v_i over every cached token of b:

@@ -119,3 +119,9 @@ def test_fp16_baseline_validates_before_any_gpu_work():
     assert call(s=-1) == 1
     assert L.ott_fp16_decode_workspace(2, 4, 1) == 0
     assert L.ott_fp16_decode_workspace(2, 4, 3) == 2 * 4 * 3 * 130 * 4
+
+
+def test_prefill_validates_before_any_gpu_work():
+    from decode_attention_ott_amd import _lib as L
+    n = (ctypes.c_int32 * 2)(10, 10)
+    assert L.lib.ott_prefill(None, None, None, n, 10, None) == 1
