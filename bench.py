@@ -26,11 +26,13 @@ if ROOT not in sys.path:
 
 METRIC = "OTT decode-attention tokens/s + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
-DECODE_SOURCES = ("decode_attention_ott_amd/csrc/ott_decode.hip",
-                  "decode_attention_ott_amd/csrc/ott_decode_gqa.hip",
-                  "decode_attention_ott_amd/csrc/ott_decode_common.h",
-                  "decode_attention_ott_amd/csrc/ott_mx.h",
-                  "decode_attention_ott_amd/csrc/ott_device.h")
+# sources of the one-head decode kernel and the split combine; the grouped-head
+# kernel adds its own file
+MHA_SOURCES = ("decode_attention_ott_amd/csrc/ott_decode.hip",
+               "decode_attention_ott_amd/csrc/ott_decode_common.h",
+               "decode_attention_ott_amd/csrc/ott_mx.h",
+               "decode_attention_ott_amd/csrc/ott_device.h")
+GQA_SOURCES = MHA_SOURCES + ("decode_attention_ott_amd/csrc/ott_decode_gqa.hip",)
 
 
 def algorithmic_decode_bytes(layer) -> int:
@@ -65,23 +67,32 @@ def decode_kernel_name(w) -> str:
     return f"decode_gqa_kernel<{w.group_size}, {na}>"
 
 
-def kernel_source_hash() -> str:
+def decode_sources(w):
+    return MHA_SOURCES if w.num_q_heads == w.num_kv_heads else GQA_SOURCES
+
+
+def kernel_source_hash(w, read=None) -> str:
+    """Hash of the sources the workload's decode kernels are built from (read(path)
+    -> bytes may supply another version of them)."""
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for p in decode_sources(w):
+        if read is None:
+            with open(os.path.join(ROOT, p), "rb") as f:
+                h.update(f.read())
+        else:
+            h.update(read(p))
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(w):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    were taken on the current source of the workload's decode kernels."""
+    path = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(w):
         return None
     return t.get("bytes_per_launch")
 
@@ -461,7 +472,7 @@ def main():
     n_dec = 5 * args.states * -(-20 // args.states)
     bytes_per_launch = sum(dec_bytes) / len(dec_bytes)
     achieved = bytes_per_launch / (dec_only_us * 1e-6) / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
