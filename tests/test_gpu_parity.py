@@ -130,6 +130,19 @@ def test_capacity_error_leaves_state_unchanged():
     assert layer.seq_state(0) == (161, 33, 128, 1)
 
 
+def test_maximum_batch_and_pool():
+    """The largest batch (512 sequences: the one-split decode deals the heads to
+    CUs by size) and the largest pool (512 > G, so the first pages have no
+    members), two query heads per KV head (a padded group), ragged lengths."""
+    w = synth.Workload("max-b512-p512", 512, 2, 1, 128, 64, 16, 512, (100, 900), 3, seed=17)
+    run_case(w, heads=[(0, 0), (137, 0), (300, 0), (511, 0)])
+
+
+def test_maximum_head_ratio():
+    """64 query heads per KV head (passes of 8 over every page)."""
+    run_case(small("ratio64", B=1, Hq=128, Hkv=2, L=(700, 700), steps=2, seed=64))
+
+
 # ---- the five layer shapes ---------------------------------------------------
 def test_llama2_7b_full():
     """32 heads, 4096 context, 64 steps with a quantize at step 32: every head."""
