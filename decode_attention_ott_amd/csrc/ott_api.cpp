@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <new>
 #include <vector>
@@ -350,6 +351,37 @@ ott_status_t ott_set_num_splits(ott_handle_t h, int32_t num_splits) {
   return OTT_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Work-groups of the fp16 baseline kernel the current device holds at once
+// (CUs x work-groups per CU), per device and heads-per-pass variant, asked of
+// the runtime once: the answer does not change while the process runs.
+int64_t fp16_decode_slots(int hg) {
+  constexpr int kDevices = 64;
+  static std::atomic<int64_t> cache[kDevices][9];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) dev = -1;
+  if (dev >= 0) {
+    const int64_t c = cache[dev][hg].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  int wpc = ott::fp16_decode_wgs_per_cu(hg);
+  if (wpc <= 0) wpc = 2;
+  const int64_t slots = int64_t(cus) * wpc;
+  if (dev >= 0) cache[dev][hg].store(slots, std::memory_order_relaxed);
+  return slots;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || num_splits <= 1) return 0;
   return size_t(batch) * num_q_heads * num_splits * (2 + ott::kHeadDim) * sizeof(float);
@@ -382,14 +414,8 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
                                                   sizeof(float)));
   int S = num_splits;
   if (S == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    int wpc = ott::fp16_decode_wgs_per_cu(num_q_heads / num_kv_heads);
-    if (wpc <= 0) wpc = 2;
-    S = int(std::max<int64_t>(1, int64_t(cus) * wpc / (int64_t(batch) * num_kv_heads)));
+    const int64_t slots = fp16_decode_slots(ott::fp16_heads_per_pass(num_q_heads / num_kv_heads));
+    S = int(std::max<int64_t>(1, slots / (int64_t(batch) * num_kv_heads)));
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, (lmax + 255) / 256)));
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, fit)));
   } else if (S > 1 && S > fit) {

@@ -149,8 +149,8 @@ int wgs_hg() {
 
 int fp16_heads_per_pass(int nq) { return nq % 8 == 0 ? 8 : nq % 4 == 0 ? 4 : nq % 2 == 0 ? 2 : 1; }
 
-int fp16_decode_wgs_per_cu(int nq) {
-  switch (fp16_heads_per_pass(nq)) {
+int fp16_decode_wgs_per_cu(int hg) {
+  switch (hg) {
     case 8: return wgs_hg<8>();
     case 4: return wgs_hg<4>();
     case 2: return wgs_hg<2>();

@@ -83,8 +83,10 @@ struct Fp16Cache {
 struct Fp16Lens {
   int32_t len[kMaxBatch];
 };
+// query heads of a KV head that share a loaded chunk (8, 4, 2 or 1)
 int fp16_heads_per_pass(int nq);
-int fp16_decode_wgs_per_cu(int nq);
+// work-groups per CU of the fp16 kernel variant for hg heads per pass
+int fp16_decode_wgs_per_cu(int hg);
 hipError_t launch_fp16_decode(const Fp16Cache& c, const Fp16Lens& lens, int num_splits,
                               hipStream_t s);
 
