@@ -134,10 +134,12 @@ class Page:
         return int(self.pos.size)
 
     def k_hat(self) -> np.ndarray:
-        return F64(self.k_min)[None, :] + F64(self.k_scale)[None, :] * self.k_code.astype(F64)
+        k_min, k_scale = np.asarray(self.k_min, F64), np.asarray(self.k_scale, F64)
+        return k_min[None, :] + k_scale[None, :] * self.k_code.astype(F64)
 
     def v_hat(self) -> np.ndarray:
-        return F64(self.v_min)[:, None] + F64(self.v_scale)[:, None] * self.v_code.astype(F64)
+        v_min, v_scale = np.asarray(self.v_min, F64), np.asarray(self.v_scale, F64)
+        return v_min[:, None] + v_scale[:, None] * self.v_code.astype(F64)
 
 
 def quantize_members(k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> Page:
@@ -162,9 +164,45 @@ def quantize_members(k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> Page:
 # State of one (sequence, KV head)
 # --------------------------------------------------------------------------
 
+# Retention rules for the outlier pool. The method keeps the tokens with the
+# smallest Key magnitude ([Abs] TL;DR and Figure 1(c), which also compares it
+# with other rules; [Blog] 3.1). The other two exist for that comparison.
+RETAIN_SMALLEST_NORM = 0
+RETAIN_LARGEST_NORM = 1
+RETAIN_RANDOM = 2
+
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int) -> int:
+    """First output of a SplitMix64 generator whose state is `seed` (the
+    generator of Steele, Lea and Flood, in the form Vigna publishes with the
+    xoshiro generators): state += 0x9E3779B97F4A7C15, then two xor-shift-multiply
+    rounds and a final xor-shift."""
+    z = (seed + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def retention_key(n2: float, pos: int, rule: int) -> float:
+    """The value the pool keeps the smallest of (ties to the lower position):
+    the squared Key norm, its negation (largest norms kept), or a random value
+    in [0, 1) drawn per position (the top 53 bits of splitmix64(pos) as a
+    fraction, exact in fp64)."""
+    if rule == RETAIN_SMALLEST_NORM:
+        return float(n2)
+    if rule == RETAIN_LARGEST_NORM:
+        return -float(n2)
+    if rule == RETAIN_RANDOM:
+        return float(splitmix64(int(pos)) >> 11) * 2.0 ** -53
+    raise ValueError(f"unknown retention rule {rule}")
+
+
 @dataclasses.dataclass
 class Entry:
     n2: float           # squared Key norm (fp64); NaN while still in the window
+    key: float          # retention key (= n2 under the method's rule); NaN in the window
     pos: int
     k: np.ndarray       # fp16 [d]
     v: np.ndarray       # fp16 [d]
@@ -173,13 +211,15 @@ class Entry:
 class HeadOracle:
     """The three caches of one (sequence, KV head) ([Blog] 3.3)."""
 
-    def __init__(self, head_dim: int, group_size: int, residual: int, pool_size: int):
+    def __init__(self, head_dim: int, group_size: int, residual: int, pool_size: int,
+                 retention: int = RETAIN_SMALLEST_NORM):
         self.d = head_dim
         self.G = group_size
         self.R = residual
         self.P = pool_size
+        self.retention = retention
         self.pages: List[Page] = []
-        self.pool: List[Entry] = []          # ascending (n2, pos)
+        self.pool: List[Entry] = []          # ascending (key, pos)
         self.recent: List[Entry] = []        # ascending pos
         self.L = 0
 
@@ -188,7 +228,8 @@ class HeadOracle:
         k_rows = np.asarray(k_rows, F16).reshape(-1, self.d)
         v_rows = np.asarray(v_rows, F16).reshape(-1, self.d)
         for i in range(k_rows.shape[0]):
-            self.recent.append(Entry(float("nan"), self.L, k_rows[i].copy(), v_rows[i].copy()))
+            self.recent.append(Entry(float("nan"), float("nan"), self.L, k_rows[i].copy(),
+                                     v_rows[i].copy()))
             self.L += 1
 
     def ready(self) -> bool:
@@ -202,7 +243,8 @@ class HeadOracle:
         1. the G oldest window tokens are the group (R4, R5);
         2. their Key norms are computed (R2);
         3. the pool and the group compete: the P smallest norms stay in the pool
-           ([Blog] 3.2), ties by position (R2);
+           ([Blog] 3.2), ties by position (R2) (other retention rules: the P
+           smallest keys of `retention_key`);
         4. everything else, evicted pool tokens included (R3), is quantized to
            2 bits as one page (R6-R8).
         """
@@ -212,7 +254,8 @@ class HeadOracle:
         norms = sq_key_norm(np.stack([e.k for e in group]))
         for e, n2 in zip(group, norms):
             e.n2 = float(n2)
-        cands = sorted(self.pool + group, key=lambda e: (e.n2, e.pos))
+            e.key = retention_key(e.n2, e.pos, self.retention)
+        cands = sorted(self.pool + group, key=lambda e: (e.key, e.pos))
         keep = min(self.P, len(cands))
         self.pool = cands[:keep]
         members = sorted(cands[keep:], key=lambda e: e.pos)
@@ -350,7 +393,8 @@ class OTTOracle:
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  group_size: int, residual: int, pool_size: int,
                  sm_scale: Optional[float] = None,
-                 heads: Optional[Iterable[Tuple[int, int]]] = None):
+                 heads: Optional[Iterable[Tuple[int, int]]] = None,
+                 retention: int = RETAIN_SMALLEST_NORM):
         assert num_q_heads % num_kv_heads == 0
         self.B, self.Hq, self.Hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
         self.G, self.R, self.P = group_size, residual, pool_size
@@ -359,13 +403,14 @@ class OTTOracle:
         if heads is None:
             heads = [(b, h) for b in range(batch) for h in range(num_kv_heads)]
         self.heads: Dict[Tuple[int, int], HeadOracle] = {
-            (int(b), int(h)): HeadOracle(head_dim, group_size, residual, pool_size)
+            (int(b), int(h)): HeadOracle(head_dim, group_size, residual, pool_size, retention)
             for b, h in heads}
 
     @classmethod
     def for_workload(cls, w, heads=None) -> "OTTOracle":
         return cls(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.group_size,
-                   w.residual, w.pool_size, heads=heads)
+                   w.residual, w.pool_size, heads=heads,
+                   retention=getattr(w, "retention", RETAIN_SMALLEST_NORM))
 
     def head(self, b: int, kvh: int) -> HeadOracle:
         return self.heads[(b, kvh)]

@@ -50,7 +50,7 @@ def check_state(layer, orc: O.OTTOracle, heads: Iterable[Tuple[int, int]], where
                 assert (ppos[n, pg.n_valid:] == -1).all(), (where, b, h, n)
         pos, n2, pk, pv = layer.pool(b, h)
         assert pos.tolist() == [e.pos for e in st.pool], (where, b, h, "pool membership")
-        assert np.array_equal(n2, np.array([e.n2 for e in st.pool], np.float64)), (where, b, h)
+        assert np.array_equal(n2, np.array([e.key for e in st.pool], np.float64)), (where, b, h)
         if st.pool:
             assert np.array_equal(pk.view(np.uint16), np.stack([e.k for e in st.pool]).view(np.uint16))
             assert np.array_equal(pv.view(np.uint16), np.stack([e.v for e in st.pool]).view(np.uint16))

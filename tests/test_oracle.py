@@ -165,6 +165,45 @@ def test_pool_is_bruteforce_topP(G, P, d):
         assert [e.pos for e in st.pool] == seen[:P]
 
 
+def test_splitmix64_matches_the_reference_outputs():
+    """The generator behind the random retention rule: seeded with 1234567, the
+    reference SplitMix64 (Vigna's public-domain splitmix64.c) yields these first
+    five outputs; each output here is splitmix64(state) with the state advanced
+    by the generator's constant between calls."""
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
+            4593380528125082431, 16408922859458223821]
+    state, got = 1234567, []
+    for _ in range(5):
+        got.append(O.splitmix64(state))
+        state = (state + 0x9E3779B97F4A7C15) & ((1 << 64) - 1)
+    assert got == want
+
+
+@pytest.mark.parametrize("rule", [O.RETAIN_LARGEST_NORM, O.RETAIN_RANDOM])
+@pytest.mark.parametrize("G,P", [(4, 3), (8, 8), (4, 9)])
+def test_other_retention_rules_are_bruteforce_topP(rule, G, P):
+    """The comparison rules of [Abs] Fig. 1(c): the pool is the P seen tokens of
+    largest exact Key norm (ties to the lower position), or of smallest random
+    key; the random key of a position is its splitmix64 value's top 53 bits,
+    compared here as integers."""
+    d, R = 4, 3
+    rng = np.random.default_rng(7 * G + P + rule)
+    k, v = _tiny_stream(12 * G + 5, d, rng)
+    exact = [_exact_sq_norm(row) for row in k]
+    st = O.HeadOracle(d, G, R, P, retention=rule)
+    for i in range(k.shape[0]):
+        O.step(st, k[i], v[i])
+        nb = len(st.pages)
+        if rule == O.RETAIN_LARGEST_NORM:
+            seen = sorted(range(G * nb), key=lambda p: (-exact[p], p))
+        else:
+            seen = sorted(range(G * nb), key=lambda p: (O.splitmix64(p) >> 11, p))
+        assert [e.pos for e in st.pool] == seen[:P]
+        # every cached token is somewhere, once
+        pos = np.concatenate([c[0] for c in st.caches()])
+        assert sorted(pos.tolist()) == list(range(st.L))
+
+
 @pytest.mark.parametrize("G,R,P", [(4, 2, 2), (8, 0, 3), (4, 5, 9), (8, 8, 0), (16, 4, 16)])
 def test_token_accounting(G, R, P):
     """Every position is in exactly one cache; pages hold G members except the
