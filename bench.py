@@ -281,8 +281,10 @@ def accuracy(args, batch: int = 8):
                               Kd.data_ptr(), Vd.data_ptr(), int(lengths.max()), lengths,
                               qd.data_ptr(), ref.data_ptr(), 0.0, work.data_ptr(), nbytes, 0, sp)
             refs[name] = (qd, ref)
-        for P in (0, 32, 128):
-            w = base.with_(pool_size=P)
+        # the method's rule at P = 0, 32, 128; the comparison rules of the pages'
+        # Figure 1(c) (largest Key norm, random) at P = 32
+        for P, rule in ((0, 0), (32, 0), (128, 0), (32, 1), (32, 2)):
+            w = base.with_(pool_size=P, retention=rule)
             lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()))
             lay.prefill(Kd, Vd, lengths)
             for name, (qd, ref) in refs.items():
@@ -296,6 +298,7 @@ def accuracy(args, batch: int = 8):
                     "accuracy": "attention output vs exact fp16-cache attention",
                     "workload": w.name, "batch": batch, "one_signed_outlier_channels": one_signed,
                     "queries": name, "G": w.group_size, "R": w.residual, "P": P,
+                    "retention": ["smallest Key norm", "largest Key norm", "random"][rule],
                     "rel_l2_total": round(float(e.norm() / r.norm()), 5),
                     "rel_l2_per_head_mean": round(float(rel.mean()), 5),
                     "rel_l2_per_head_max": round(float(rel.max()), 5),

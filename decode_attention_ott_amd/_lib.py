@@ -31,7 +31,7 @@ class ott_config_t(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("residual", ctypes.c_int32),
                 ("pool_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
-                ("sm_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("retention", ctypes.c_int32)]
 
 
 class ott_layout_t(ctypes.Structure):

@@ -38,6 +38,8 @@ ott_status_t validate_config(const ott_config_t* c) {
     return OTT_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return OTT_ERR_INVALID_ARG;
   if (!(c->sm_scale == c->sm_scale)) return OTT_ERR_INVALID_ARG;  // NaN
+  if (c->retention < OTT_RETAIN_SMALLEST_NORM || c->retention > OTT_RETAIN_RANDOM)
+    return OTT_ERR_INVALID_ARG;
   if (c->batch > ott::kMaxBatch) return OTT_ERR_UNSUPPORTED;
   if (c->head_dim != ott::kHeadDim) return OTT_ERR_UNSUPPORTED;
   if (c->group_size != 64 && c->group_size != 128 && c->group_size != 256)
@@ -153,6 +155,7 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   a.off_partials = lay.off_partials;
   a.off_split_sync = lay.off_split_sync;
   a.sm_scale = h->cfg.sm_scale;
+  a.retention = h->cfg.retention;
   const size_t nb = size_t(cfg->batch);
   h->L.assign(nb, 0);
   h->rcnt.assign(nb, 0);

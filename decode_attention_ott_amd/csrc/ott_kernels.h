@@ -22,6 +22,7 @@ struct Arena {
   uint64_t off_pool_k, off_pool_v, off_pool_pos, off_pool_n2;
   uint64_t off_ring_k, off_ring_v, off_partials, off_split_sync;
   float sm_scale;
+  int32_t retention;  // pool rule: 0 smallest squared Key norm, 1 largest, 2 random per position
 };
 
 // New-token counts of one ott_append call and the window slot of each

@@ -79,6 +79,21 @@ __device__ __forceinline__ uint32_t qcode(float x, const CodeThr& q) {
   return uint32_t(d > q.t1) + uint32_t(d >= q.t2) + uint32_t(d > q.t3);
 }
 
+// The pool's ranking key of a candidate (keys ascend, ties to the lower
+// position): the squared Key norm (the method's rule), its negation, or a
+// random fraction per position from the SplitMix64 generator.
+__device__ __forceinline__ double retention_key(double n2, int pos, int rule) {
+  if (rule == 1) return -n2;
+  if (rule == 2) {
+    uint64_t z = uint64_t(pos) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return double(z >> 11) * 0x1p-53;
+  }
+  return n2;
+}
+
 constexpr int kStageRows = 128;  // member rows staged in LDS at a time (32 KiB)
 constexpr int kQuantThreads = 1024;  // 16 waves: 4 per SIMD of the CU
 constexpr int kMinMaxParts = kQuantThreads / D;  // partial K min/max per channel
@@ -175,7 +190,7 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
           acc = acc + hi * hi;
         }
       }
-      s.n2[i] = acc;
+      s.n2[i] = retention_key(acc, G * nb + j, a.retention);
       s.pos[i] = G * nb + j;
       s.src[i] = slot | kRingFlag;
     }

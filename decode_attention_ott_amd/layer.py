@@ -24,9 +24,10 @@ def _stream() -> int:
 class OTTLayer:
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int = 128,
                  group_size: int = 128, residual: int = 32, pool_size: int = 32,
-                 max_seq_len: int = 4096, sm_scale: float = 0.0, device="cuda"):
+                 max_seq_len: int = 4096, sm_scale: float = 0.0, device="cuda",
+                 retention: int = 0):
         self.cfg = L.ott_config_t(batch, num_q_heads, num_kv_heads, head_dim, group_size,
-                                  residual, pool_size, max_seq_len, sm_scale)
+                                  residual, pool_size, max_seq_len, sm_scale, retention)
         self.B, self.Hq, self.Hkv, self.d = batch, num_q_heads, num_kv_heads, head_dim
         self.G, self.R, self.P = group_size, residual, pool_size
         self.max_seq_len = max_seq_len
@@ -44,6 +45,7 @@ class OTTLayer:
     def for_workload(cls, w, max_seq_len: Optional[int] = None, **kw) -> "OTTLayer":
         if max_seq_len is None:
             max_seq_len = w.max_prefill + w.steps
+        kw.setdefault("retention", getattr(w, "retention", 0))
         return cls(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.group_size,
                    w.residual, w.pool_size, max_seq_len, **kw)
 

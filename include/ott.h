@@ -62,7 +62,23 @@ typedef struct {
   int32_t pool_size;    /* P, 0..512: outlier-pool capacity (0 = plain 2-bit cache) */
   int32_t max_seq_len;  /* tokens a sequence may reach, >= 1 */
   float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t retention;    /* which tokens the pool keeps: OTT_RETAIN_* (0 = the method's rule) */
 } ott_config_t;
+
+/*
+ * Pool retention rules. The method keeps the P tokens with the smallest Key
+ * magnitude ([Abs] TL;DR and Figure 1(c); [Blog] 3.1): squared L2 norm, fp64,
+ * summed over channels 0..d-1. Figure 1(c) compares that choice with others; two
+ * are built for that comparison. Each candidate gets a key and the pool keeps
+ * the P smallest keys, ties to the lower position:
+ *   OTT_RETAIN_SMALLEST_NORM  key = squared norm
+ *   OTT_RETAIN_LARGEST_NORM   key = -squared norm
+ *   OTT_RETAIN_RANDOM         key = (splitmix64(position) >> 11) * 2^-53, where
+ *                             splitmix64(s) is the first output of a SplitMix64
+ *                             generator with state s (Vigna's reference form)
+ * pool_n2 holds the keys.
+ */
+enum { OTT_RETAIN_SMALLEST_NORM = 0, OTT_RETAIN_LARGEST_NORM = 1, OTT_RETAIN_RANDOM = 2 };
 
 /*
  * Arena map (byte offsets from the arena base; every region is 256-byte aligned).
@@ -81,9 +97,10 @@ typedef struct {
  *   page_nvalid int32 [B*Hkv][NB]: members per page; tests only
  *   pool_k, pool_v   fp16  [2][B*Hkv][P][d]
  *   pool_pos         int32 [2][B*Hkv][P]
- *   pool_n2          fp64  [2][B*Hkv][P]   squared Key norm of each pool token
+ *   pool_n2          fp64  [2][B*Hkv][P]   retention key of each pool token (its squared Key
+ *                                          norm under the method's rule)
  *              two buffers: after nb quantize steps the live pool is buffer (nb & 1);
- *              its first min(P, G*nb) slots are used, ascending (norm, position).
+ *              its first min(P, G*nb) slots are used, ascending (key, position).
  *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
  *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
  *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}.

@@ -61,6 +61,7 @@ class Workload:
     tok_scale: float = 0.05
     n_outlier_channels: int = 4
     one_signed: bool = False
+    retention: int = 0     # pool rule (0: the method's smallest Key norm); not an input law
 
     @property
     def max_prefill(self) -> int:

@@ -130,6 +130,16 @@ def test_capacity_error_leaves_state_unchanged():
     assert layer.seq_state(0) == (161, 33, 128, 1)
 
 
+@pytest.mark.parametrize("rule", [1, 2])
+@pytest.mark.parametrize("G,R,P,Hq,steps", [(128, 32, 32, 2, 4), (64, 16, 8, 8, 70)])
+def test_other_retention_rules(rule, G, R, P, Hq, steps):
+    """Pool kept by largest Key norm (1) or a random key per position (2): the
+    same bit-exact pool, pages and window as the oracle under that rule."""
+    w = small(f"retain{rule}-g{G}h{Hq}", Hq=Hq, G=G, R=R, P=P, L=(700, 700), steps=steps,
+              seed=10 * rule + G).with_(retention=rule)
+    run_case(w, state_every_step=True)
+
+
 def test_maximum_batch_and_pool():
     """The largest batch (512 sequences: the one-split decode deals the heads to
     CUs by size) and the largest pool (512 > G, so the first pages have no
