@@ -104,7 +104,9 @@ enum { OTT_RETAIN_SMALLEST_NORM = 0, OTT_RETAIN_LARGEST_NORM = 1, OTT_RETAIN_RAN
  *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
  *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
  *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}.
- *   split_sync int32 [B][Hq]: arrival counters of the split-K merge; zero between calls.
+ *   split_sync int32 [B][Hq]: reserved for arrival counters of an in-kernel split merge;
+ *              zeroed by ott_init and not used by the current kernels (a second kernel merges
+ *              the splits).
  */
 typedef struct {
   uint64_t arena_bytes;
