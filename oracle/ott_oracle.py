@@ -45,6 +45,16 @@ Readings taken where the pages are silent:
   R12 the pool keeps both K and V in fp16.
   R13 with grouped-query attention the caches are per KV head.
   R14 the pool keeps min(P, #candidates) entries; a page may hold fewer than G.
+  R16 the comparison rules of [Abs] Fig. 1(c), built for the accuracy measurement:
+      largest squared norm, or a random key per position (SplitMix64).
+
+What pins this module (tests/test_oracle.py): hand-derived quantizer cases,
+the quantizer's error bound and nearest-level brute force, fp16 rounding
+against Python's struct, brute-force top-P pool membership for every rule,
+the SplitMix64 reference outputs, token accounting, and reductions of the
+decode to textbook attention (no quantization, lossless grids, permutation
+and shift invariance, closed forms). Parity with the paper's own arithmetic
+is unpinned: the pages print no worked example, no codes and no outputs.
 """
 from __future__ import annotations
 
