@@ -88,6 +88,12 @@ def test_mistral_gqa_sampled():
     _run(w, synth.prefill_lengths(w), splits=[0], heads=[(0, 0), (3, 17), (7, 31)])
 
 
+def test_llama2_13b_128k_sampled():
+    """One sequence of 131072 tokens, 40 heads: many splits per head."""
+    w = synth.WORKLOADS["llama2-13b-128k"]
+    _run(w, synth.prefill_lengths(w), splits=[0, 64], heads=[(0, 0), (0, 39)])
+
+
 def test_bad_arguments_are_rejected():
     import torch
     from decode_attention_ott_amd import _lib as L, OttError
