@@ -171,3 +171,30 @@ def test_mistral_gqa_sampled():
 
 def test_llama2_13b_128k_sampled():
     run_case(W["llama2-13b-128k"], heads=[(0, 0), (0, 23), (0, 39)], steps=6)
+
+
+# ---- seeded random configurations ---------------------------------------------
+def _random_configs(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([64, 128, 256]))
+        R = int(rng.choice([0, 1, 7, 32, 64]))
+        P = int(rng.choice([0, 1, 5, 32, 100, G + 7]))
+        Hkv = int(rng.integers(1, 4))
+        nq = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(1, 4 * G + R + 40, size=B)]
+        steps = int(rng.integers(1, 83))
+        splits = [0, int(rng.integers(1, 9))]
+        out.append((i, G, R, P, Hkv, nq, B, lengths, steps, splits))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_configs(), ids=lambda c: f"rand{c[0]}")
+def test_random_configurations(case):
+    """Seeded draws over G, R, P, heads, ratio, batch, ragged lengths (from 1),
+    step counts that cross quantize steps, and split counts."""
+    i, G, R, P, Hkv, nq, B, lengths, steps, splits = case
+    w = synth.Workload(f"rand{i}", B, Hkv * nq, Hkv, 128, G, R, P, (1, 1), steps, seed=500 + i)
+    run_case(w, lengths=lengths, splits=splits, state_every_step=steps <= 16)
