@@ -263,7 +263,10 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
   if (!any) return OTT_OK;
   if (!d_k || !d_v || (reinterpret_cast<uintptr_t>(d_k) & 15) || (reinterpret_cast<uintptr_t>(d_v) & 15))
     return OTT_ERR_INVALID_ARG;
-  st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens,
+  int max_pages = 0;
+  for (int b = 0; b < B; ++b)
+    if (h_len[b] >= R + G) max_pages = std::max(max_pages, (h_len[b] - R) / G);
+  st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens, max_pages,
                                            static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
   for (int b = 0; b < B; ++b) {

@@ -56,9 +56,10 @@ hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t 
 struct PrefillLens {
   int32_t len[kMaxBatch];
 };
-// k, v: fp16 [B][Hkv][max_len][D]; the cache must be empty.
+// k, v: fp16 [B][Hkv][max_len][D]; the cache must be empty; max_pages is the
+// largest page count of any sequence (floor((L - R) / G) for L >= R + G).
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
-                          const PrefillLens& lens, hipStream_t s);
+                          const PrefillLens& lens, int max_pages, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
                          const HeadOrder& order, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it

@@ -7,7 +7,8 @@
 //   append_kernel    fp16 window update ([Blog] 3.3, residual window)
 //   quantize_kernel  quantization stage: Key norms, pool competition, 2-bit
 //                    pages ([Blog] 3.1, 3.2, flowchart; [Abs] Fig. 2 bottom)
-//   prefill_kernel   a whole prompt through the same steps, in order, in one launch
+//   prefill_select_kernel, prefill_pack_kernel  a whole prompt through the same
+//                    steps: the pool walk per head in order, then every page at once
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -112,6 +113,14 @@ struct QuantLds {
   int* mem;
 };
 
+// Dynamic LDS bytes of the QuantLds layout for (G, P).
+__host__ __device__ inline size_t quant_lds_bytes(int G, int P) {
+  const size_t nc = size_t(P) + G;
+  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
+         2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
+         G * sizeof(int);
+}
+
 __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
   QuantLds q;
   q.stage = reinterpret_cast<__half*>(base);
@@ -139,37 +148,24 @@ __device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, R
   }
 }
 
-// One quantize step of (sequence, KV head) bh: the group's G tokens are rows
-// (g_head + j) % g_mod of gk/gv (the window ring, or a prompt), competing with
-// the pool of buffer nb & 1; writes page nb, the new pool into the other
-// buffer and the page's member list. Counters are the caller's.
-__device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
-                                              const __half* __restrict__ gk,
-                                              const __half* __restrict__ gv, int g_head,
-                                              int g_mod, uint8_t* lds_raw) {
+// Steps 1-3 of a quantize step for page nb: candidates (the pool's keys and
+// positions from pkey/ppos, then the group's G tokens, rows (g_head + j) %
+// g_mod of gk), their retention keys, ranks and the members in position order,
+// all in LDS (s). The caller finishes the step.
+__device__ __forceinline__ void select_step(const Arena& a, int nb, const double* pkey,
+                                            const int32_t* ppos, const __half* __restrict__ gk,
+                                            int g_head, int g_mod, const QuantLds& s) {
   const int G = a.G, P = a.P;
   const int tid = threadIdx.x;
   const int pc = min(P, G * nb);  // pool tokens before this step
   const int NC = pc + G;          // candidates: pool + group
   const int npc = min(P, NC);     // pool tokens after this step
-  const int n_valid = NC - npc;   // page members
-  const int cur = nb & 1, nxt = cur ^ 1;
-  QuantLds s = quant_lds(lds_raw, P + G, G);
-
-  const __half* pk = pool_k(a, cur, bh);
-  const __half* pv = pool_v(a, cur, bh);
-  auto krow = [&](int src) -> const __half* {
-    return (src & kRingFlag) ? gk + size_t(src & ~kRingFlag) * D : pk + size_t(src) * D;
-  };
-  auto vrow = [&](int src) -> const __half* {
-    return (src & kRingFlag) ? gv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
-  };
 
   // 1. candidates; squared Key norms of the group, fp64 in channel order
   for (int i = tid; i < NC; i += blockDim.x) {
     if (i < pc) {
-      s.n2[i] = pool_n2(a, cur, bh)[i];
-      s.pos[i] = pool_pos(a, cur, bh)[i];
+      s.n2[i] = pkey[i];
+      s.pos[i] = ppos[i];
       s.src[i] = i;
     } else {
       const int j = i - pc;
@@ -237,8 +233,16 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
   for (int i = tid; i < NC; i += blockDim.x)
     if (s.rank[i] >= npc) s.mem[s.idx[i]] = i;
   __syncthreads();
+}
 
-  uint8_t* pg = page_ptr(a, bh, nb);
+// Steps 4-6 of a quantize step: the page pg from its n_valid members (s.mem
+// in position order, rows krow(s.src[m]) and vrow(s.src[m])): Key (min, scale)
+// per channel and codes, Value (min, scale) per member and codes, zero padding.
+template <typename KRow, typename VRow>
+__device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const QuantLds& s,
+                                          int n_valid, KRow krow, VRow vrow) {
+  const int G = a.G;
+  const int tid = threadIdx.x;
   const int n_chunks = (n_valid + kStageRows - 1) / kStageRows;
   // 4. Key (min, scale) per channel over the members: kMinMaxParts partial
   //    scans per channel, then one thread per channel combines them
@@ -361,6 +365,35 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
     for (int w = tid; w < D * (vdw - jfirst); w += blockDim.x)
       vc[(w / (vdw - jfirst)) * vdw + jfirst + w % (vdw - jfirst)] = 0u;
   }
+}
+
+// One quantize step of (sequence, KV head) bh: the group's G tokens are rows
+// (g_head + j) % g_mod of gk/gv (the window ring, or a prompt), competing with
+// the pool of buffer nb & 1; writes page nb, the new pool into the other
+// buffer and the page's member list. Counters are the caller's.
+__device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
+                                              const __half* __restrict__ gk,
+                                              const __half* __restrict__ gv, int g_head,
+                                              int g_mod, uint8_t* lds_raw) {
+  const int G = a.G, P = a.P;
+  const int tid = threadIdx.x;
+  const int pc = min(P, G * nb);
+  const int NC = pc + G;
+  const int npc = min(P, NC);
+  const int n_valid = NC - npc;
+  const int cur = nb & 1, nxt = cur ^ 1;
+  QuantLds s = quant_lds(lds_raw, P + G, G);
+
+  const __half* pk = pool_k(a, cur, bh);
+  const __half* pv = pool_v(a, cur, bh);
+  auto krow = [&](int src) -> const __half* {
+    return (src & kRingFlag) ? gk + size_t(src & ~kRingFlag) * D : pk + size_t(src) * D;
+  };
+  auto vrow = [&](int src) -> const __half* {
+    return (src & kRingFlag) ? gv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
+  };
+  select_step(a, nb, pool_n2(a, cur, bh), pool_pos(a, cur, bh), gk, g_head, g_mod, s);
+  pack_page(a, page_ptr(a, bh, nb), s, n_valid, krow, vrow);
   // 8. the new pool, slot = rank, into the other buffer
   __half* nk = pool_k(a, nxt, bh);
   __half* nv = pool_v(a, nxt, bh);
@@ -406,44 +439,125 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
 // prefill: a prompt of L_b tokens per sequence into an empty cache, with the
 // same result as appending it and running every due quantize step in order.
 // A window is full at R+G tokens and a step removes G, so the prompt makes
-// nq = floor((L - R) / G) pages (0 when L < R + G): one work-group per
-// (sequence, KV head) runs the steps in position order (each step's pool is
-// the previous step's), then the last L - G nq tokens form the window, whose
-// head slot is where G nq single steps would have left it.
+// nq = floor((L - R) / G) pages (0 when L < R + G). Two kernels:
+//   prefill_select_kernel  one work-group per (sequence, KV head) walks the
+//       groups in position order on keys alone (the pool's keys and positions
+//       stay in LDS from step to step): each step's members go to the page's
+//       member list; then the final pool and the one before it (the two pool
+//       buffers single steps would leave) and the window.
+//   prefill_pack_kernel    one work-group per page: the page bytes from its
+//       members' rows, read from the prompt by position.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kQuantThreads) void prefill_kernel(Arena a,
-                                                                const __half* __restrict__ k,
-                                                                const __half* __restrict__ v,
-                                                                int64_t max_len, PrefillLens lens) {
+__device__ __forceinline__ int prefill_pages(const Arena& a, int L) {
+  return L >= a.R + a.G ? (L - a.R) / a.G : 0;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
+    Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
+    PrefillLens lens) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const int h = blockIdx.x, b = blockIdx.y;
   const int bh = b * a.Hkv + h;
   const int L = lens.len[b];
   if (L == 0) return;
-  const int G = a.G, C = a.C;
-  const int nq = L >= a.R + G ? (L - a.R) / G : 0;
+  const int G = a.G, P = a.P, C = a.C;
+  const int tid = threadIdx.x;
+  const int nq = prefill_pages(a, L);
   const __half* kb = k + size_t(bh) * max_len * D;
   const __half* vb = v + size_t(bh) * max_len * D;
-  for (int n = 0; n < nq; ++n)
-    quantize_step(a, bh, n, kb + size_t(n) * G * D, vb + size_t(n) * G * D, 0, G, lds_raw);
+  QuantLds s = quant_lds(lds_raw, P + G, G);
+  // two pools of keys and positions after the QuantLds region
+  double* pkey[2];
+  int32_t* ppos[2];
+  {
+    uint8_t* base = lds_raw + ((quant_lds_bytes(G, P) + 15) & ~size_t(15));
+    pkey[0] = reinterpret_cast<double*>(base);
+    pkey[1] = pkey[0] + P;
+    ppos[0] = reinterpret_cast<int32_t*>(pkey[1] + P);
+    ppos[1] = ppos[0] + P;
+  }
+  int32_t* page_pos_all = reinterpret_cast<int32_t*>(a.base + a.off_page_pos);
+  int32_t* page_nv_all = reinterpret_cast<int32_t*>(a.base + a.off_page_nvalid);
+  for (int n = 0; n < nq; ++n) {
+    const int pc = min(P, G * n), NC = pc + G, npc = min(P, NC), n_valid = NC - npc;
+    const int cur = n & 1;
+    select_step(a, n, pkey[cur], ppos[cur], kb + size_t(n) * G * D, 0, G, s);
+    int32_t* pp = page_pos_all + (size_t(bh) * a.nb_max + n) * G;
+    for (int t = tid; t < G; t += blockDim.x) pp[t] = t < n_valid ? s.pos[s.mem[t]] : -1;
+    if (tid == 0) page_nv_all[size_t(bh) * a.nb_max + n] = n_valid;
+    for (int i = tid; i < NC; i += blockDim.x) {
+      const int r = s.rank[i];
+      if (r < npc) {
+        pkey[cur ^ 1][r] = s.n2[i];
+        ppos[cur ^ 1][r] = s.pos[i];
+      }
+    }
+    __syncthreads();
+  }
+  // pools: after nq steps in buffer nq & 1, after nq - 1 steps in the other one
+  for (int back = 0; back < 2 && back < nq; ++back) {
+    const int steps = nq - back, buf = steps & 1;
+    const int cnt = min(P, G * steps);
+    __half* dk = pool_k(a, buf, bh);
+    __half* dv = pool_v(a, buf, bh);
+    for (int w = tid; w < cnt * (D / 8); w += blockDim.x) {
+      const int i = w / (D / 8), c8 = w % (D / 8);
+      const int pos = ppos[buf][i];
+      reinterpret_cast<uint4*>(dk + size_t(i) * D)[c8] =
+          reinterpret_cast<const uint4*>(kb + size_t(pos) * D)[c8];
+      reinterpret_cast<uint4*>(dv + size_t(i) * D)[c8] =
+          reinterpret_cast<const uint4*>(vb + size_t(pos) * D)[c8];
+      if (c8 == 0) {
+        pool_pos(a, buf, bh)[i] = pos;
+        pool_n2(a, buf, bh)[i] = pkey[buf][i];
+      }
+    }
+  }
+  // the window: the last L - G nq tokens, at the slots single steps would use
   const int rc = L - G * nq, head = (G * nq) % C;
   uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
   uint4* rv = reinterpret_cast<uint4*>(ring_v(a, bh));
   const uint4* sk = reinterpret_cast<const uint4*>(kb + size_t(G) * nq * D);
   const uint4* sv = reinterpret_cast<const uint4*>(vb + size_t(G) * nq * D);
-  for (int i = threadIdx.x; i < rc * (D / 8); i += blockDim.x) {
+  for (int i = tid; i < rc * (D / 8); i += blockDim.x) {
     const int t = i / (D / 8), c = i % (D / 8);
     const int slot = (head + t) % C;
     rk[size_t(slot) * (D / 8) + c] = sk[i];
     rv[size_t(slot) * (D / 8) + c] = sv[i];
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int32_t* ctr = counters(a, bh);
     ctr[0] = L;
     ctr[1] = rc;
     ctr[2] = head;
     ctr[3] = nq;
   }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void prefill_pack_kernel(
+    Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
+    PrefillLens lens) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.Hkv + h;
+  const int L = lens.len[b];
+  if (n >= prefill_pages(a, L)) return;
+  const int G = a.G, P = a.P;
+  const int pc = min(P, G * n);
+  const int n_valid = pc + G - min(P, pc + G);
+  const __half* kb = k + size_t(bh) * max_len * D;
+  const __half* vb = v + size_t(bh) * max_len * D;
+  QuantLds s = quant_lds(lds_raw, P + G, G);
+  const int32_t* pp = reinterpret_cast<const int32_t*>(a.base + a.off_page_pos) +
+                      (size_t(bh) * a.nb_max + n) * G;
+  for (int t = threadIdx.x; t < n_valid; t += blockDim.x) {
+    s.src[t] = pp[t];  // a position in the prompt
+    s.mem[t] = t;
+  }
+  __syncthreads();
+  auto krow = [&](int pos) -> const __half* { return kb + size_t(pos) * D; };
+  auto vrow = [&](int pos) -> const __half* { return vb + size_t(pos) * D; };
+  pack_page(a, page_ptr(a, bh, n), s, n_valid, krow, vrow);
 }
 
 }  // namespace
@@ -456,24 +570,35 @@ hipError_t launch_append(const Arena& a, const void* k, const void* v, const App
   return hipGetLastError();
 }
 
-size_t quantize_lds_bytes(int G, int P) {
-  using dev::D;
-  const size_t nc = size_t(P) + G;
-  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
-         2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
-         G * sizeof(int);
+size_t quantize_lds_bytes(int G, int P) { return quant_lds_bytes(G, P); }
+
+size_t prefill_select_lds_bytes(int G, int P) {
+  return ((quant_lds_bytes(G, P) + 15) & ~size_t(15)) + size_t(P) * 2 * (sizeof(double) + 4);
 }
 
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
-                          const PrefillLens& lens, hipStream_t s) {
+                          const PrefillLens& lens, int max_pages, hipStream_t s) {
+  const size_t lds_sel = prefill_select_lds_bytes(a.G, a.P);
   const size_t lds = quantize_lds_bytes(a.G, a.P);
+  if (lds_sel > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_select_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int(lds_sel));
+    if (e != hipSuccess) return e;
+  }
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_pack_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prefill_kernel, dim3(a.Hkv, a.B), dim3(kQuantThreads), lds, s, a,
-                     static_cast<const __half*>(k), static_cast<const __half*>(v), max_len, lens);
+  const __half* kh = static_cast<const __half*>(k);
+  const __half* vh = static_cast<const __half*>(v);
+  hipLaunchKernelGGL(prefill_select_kernel, dim3(a.Hkv, a.B), dim3(kQuantThreads), lds_sel, s, a,
+                     kh, vh, max_len, lens);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_pages == 0) return e;
+  hipLaunchKernelGGL(prefill_pack_kernel, dim3(max_pages, a.Hkv, a.B), dim3(kQuantThreads), lds, s,
+                     a, kh, vh, max_len, lens);
   return hipGetLastError();
 }
 
