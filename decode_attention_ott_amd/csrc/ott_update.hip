@@ -111,6 +111,7 @@ struct QuantLds {
   int* rank;
   int* idx;       // member index of a candidate (counting)
   int* mem;
+  int* wsum;      // [16] per-wave member counts of the group
 };
 
 // Dynamic LDS bytes of the QuantLds layout for (G, P).
@@ -118,7 +119,7 @@ __host__ __device__ inline size_t quant_lds_bytes(int G, int P) {
   const size_t nc = size_t(P) + G;
   return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
          2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
-         G * sizeof(int);
+         G * sizeof(int) + 16 * sizeof(int);
 }
 
 __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
@@ -134,6 +135,7 @@ __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
   q.rank = q.src + NCmax;
   q.idx = q.rank + NCmax;
   q.mem = q.idx + NCmax;
+  q.wsum = q.mem + G;
   return q;
 }
 
@@ -193,40 +195,84 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
   }
   __syncthreads();
 
-  // 2. rank under (norm, position): each candidate's comparisons are split
-  //    over `parts` threads (branch-free, so the LDS reads pipeline) and the
-  //    counts summed with LDS atomics
+  // 2. rank under (key, position). The pool's entries (i < pc) are in
+  //    ascending (key, position) order and every pool position precedes every
+  //    group position, so a pool entry's rank is its index plus the group keys
+  //    below its key, and a group token's rank is the pool keys at or below its
+  //    key (a binary search) plus the group tokens below it. The comparisons
+  //    against the group are split over `parts` threads per candidate
+  //    (branch-free, so the LDS reads pipeline) and summed with LDS atomics.
   const int parts = max(1, int(blockDim.x) / NC);
-  const int span = (NC + parts - 1) / parts;
+  const int span = (G + parts - 1) / parts;
   for (int i = tid; i < NC; i += blockDim.x) {
     s.rank[i] = 0;
     s.idx[i] = 0;
   }
   __syncthreads();
   for (int x = tid; x < NC * parts; x += blockDim.x) {
-    const int i = x % NC, j0 = (x / NC) * span, j1 = min(NC, j0 + span);
+    const int i = x % NC, part = x / NC;
+    const int j0 = pc + part * span, j1 = min(NC, j0 + span);
     const double ni = s.n2[i];
     const int pi = s.pos[i];
     int r = 0;
+    if (i < pc) {
 #pragma unroll 4
-    for (int j = j0; j < j1; ++j) {
-      const double nj = s.n2[j];
-      const int pj = s.pos[j];
-      r += int(nj < ni) | (int(nj == ni) & int(pj < pi));
+      for (int j = j0; j < j1; ++j) r += int(s.n2[j] < ni);
+      if (part == 0) r += i;
+    } else {
+#pragma unroll 4
+      for (int j = j0; j < j1; ++j) {
+        const double nj = s.n2[j];
+        const int pj = s.pos[j];
+        r += int(nj < ni) | (int(nj == ni) & int(pj < pi));
+      }
+      if (part == 0) {  // pool keys <= ni
+        int lo = 0, hi = pc;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s.n2[mid] <= ni) lo = mid + 1; else hi = mid;
+        }
+        r += lo;
+      }
     }
-    atomicAdd(&s.rank[i], r);
+    if (r) atomicAdd(&s.rank[i], r);
   }
   __syncthreads();
 
-  // 3. members (rank >= npc) in position order, counted the same way
-  for (int x = tid; x < NC * parts; x += blockDim.x) {
-    const int i = x % NC, j0 = (x / NC) * span, j1 = min(NC, j0 + span);
-    if (s.rank[i] >= npc) {
-      const int pi = s.pos[i];
-      int c = 0;
+  // 3. members (rank >= npc) in position order: the evicted pool entries come
+  //    first (their positions precede the group's), ordered by position among
+  //    themselves; the group's members follow in group order (a prefix count
+  //    of the member flags, by wave ballots)
+  {
+    const int pparts = pc > 0 ? max(1, int(blockDim.x) / pc) : 1;
+    const int pspan = pc > 0 ? (pc + pparts - 1) / pparts : 0;
+    for (int x = tid; x < pc * pparts; x += blockDim.x) {
+      const int i = x % pc, j0 = (x / pc) * pspan, j1 = min(pc, j0 + pspan);
+      if (s.rank[i] >= npc) {
+        const int pi = s.pos[i];
+        int c = 0;
 #pragma unroll 4
-      for (int j = j0; j < j1; ++j) c += int(s.rank[j] >= npc) & int(s.pos[j] < pi);
-      atomicAdd(&s.idx[i], c);
+        for (int j = j0; j < j1; ++j) c += int(s.rank[j] >= npc) & int(s.pos[j] < pi);
+        if (c) atomicAdd(&s.idx[i], c);
+      }
+    }
+    // group token g = tid (< G <= 256: the first G / 64 waves)
+    const bool in_group = tid < G;
+    const bool mflag = in_group && s.rank[pc + tid] >= npc;
+    const uint64_t ball = __ballot(mflag);
+    const int lane = tid & 63, wv = tid >> 6;
+    const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(ball >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(uint32_t(ball), 0));
+    if (lane == 0 && tid < G) s.wsum[wv] = __popcll(ball);
+    __syncthreads();
+    if (mflag) {
+      int before = 0, total = 0;
+      for (int w = 0; w < (G + 63) / 64; ++w) {
+        total += s.wsum[w];
+        if (w < wv) before += s.wsum[w];
+      }
+      const int n_evicted = (NC - npc) - total;
+      s.idx[pc + tid] = n_evicted + before + below;
     }
   }
   __syncthreads();
