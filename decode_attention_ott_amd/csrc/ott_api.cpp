@@ -49,6 +49,7 @@ ott_status_t validate_config(const ott_config_t* c) {
   if (nq > 64) return OTT_ERR_UNSUPPORTED;
   const int64_t heads = int64_t(c->batch) * c->num_kv_heads;
   if (heads > (1 << 20)) return OTT_ERR_UNSUPPORTED;
+  if (c->num_kv_heads > 65535) return OTT_ERR_UNSUPPORTED;  // a grid dimension of the prefill
   return OTT_OK;
 }
 

@@ -55,7 +55,7 @@ typedef enum {
 typedef struct {
   int32_t batch;        /* B, 1..512 */
   int32_t num_q_heads;  /* Hq, a multiple of Hkv with Hq/Hkv <= 64 */
-  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t num_kv_heads; /* Hkv, 1..65535; B * Hkv <= 2^20 */
   int32_t head_dim;     /* d, must be 128 */
   int32_t group_size;   /* G: tokens per quantized group, 64, 128 or 256 */
   int32_t residual;     /* R >= 0: tokens always kept in the fp16 window */

@@ -69,6 +69,7 @@ def test_any_head_ratio_up_to_64_is_accepted():
     (dict(batch=0), 1), (dict(batch=513), 2), (dict(pool_size=-1), 1), (dict(pool_size=600), 2),
     (dict(residual=-1), 1), (dict(max_seq_len=0), 1), (dict(sm_scale=float("nan")), 1),
     (dict(retention=3), 1), (dict(retention=-1), 1),
+    (dict(batch=1, num_q_heads=65536, num_kv_heads=65536), 2),
 ])
 def test_bad_configs_are_rejected(bad, status):
     st, _ = _sizing(_cfg(**bad))
