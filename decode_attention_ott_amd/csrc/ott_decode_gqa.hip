@@ -189,13 +189,22 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
     const i32x8 aq = gx_a<G>(L.qa(a), lane);
-    // all tiles issued before any result is read, so the products overlap
-    f32x4v zr[NT];
+    if constexpr (NT <= 8) {
+      // all tiles issued before any result is read, so the products overlap
+      f32x4v zr[NT];
 #pragma unroll
-    for (int T = 0; T < NT; ++T)
-      zr[T] = mx_mfma<0>(aq, mx_b(r.kc[T]), f32x4v{0.f, 0.f, 0.f, 0.f}, sq[a]);
+      for (int T = 0; T < NT; ++T)
+        zr[T] = mx_mfma<0>(aq, mx_b(r.kc[T]), f32x4v{0.f, 0.f, 0.f, 0.f}, sq[a]);
 #pragma unroll
-    for (int T = 0; T < NT; ++T) z[a][T] = bias[a] + ((zr[T][0] + zr[T][1]) + (zr[T][2] + zr[T][3]));
+      for (int T = 0; T < NT; ++T)
+        z[a][T] = bias[a] + ((zr[T][0] + zr[T][1]) + (zr[T][2] + zr[T][3]));
+    } else {  // G = 256: 16 live results would not fit beside the page
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        const f32x4v zr = mx_mfma<0>(aq, mx_b(r.kc[T]), f32x4v{0.f, 0.f, 0.f, 0.f}, sq[a]);
+        z[a][T] = bias[a] + ((zr[0] + zr[1]) + (zr[2] + zr[3]));
+      }
+    }
   }
   if (n_valid < G) {
 #pragma unroll
