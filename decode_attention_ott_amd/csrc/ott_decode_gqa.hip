@@ -18,11 +18,13 @@
 // Result row 4h + k then sits in lane group h, so every lane group owns one
 // head of the group: its scores, its softmax state and its value sums.
 //
-// Token order of the score tiles. Column j of K tile T (block b = T / NTB,
-// t = T % NTB) is the token of logical slot k = NTB j + t of value block b, so
-// a lane's NTB scores are NTB consecutive logical slots of the value operand:
-// each digit row of p' leaves the lane as one 8-byte (G >= 128) or 4-byte
-// (G = 64) LDS write.
+// Token order of the score tiles. K tile T holds the 16 consecutive tokens
+// 16T..16T+15, column j the one at logical slot 16T + j of the value operand
+// (token 16T + mx_item(j)), so each load of a tile's codes reads whole cache
+// lines that no other load of the page touches. A lane's scores then sit at
+// one slot in each 16-slot stretch; a 4 x 4 byte transpose inside each quad of
+// lanes turns every 4 tiles of a digit row of p' into one 4-byte LDS write per
+// lane.
 #include "ott_decode_common.h"
 #include "ott_mx.h"
 
@@ -40,11 +42,19 @@ struct Gx {
   static constexpr int ABLK = 16 * RS;               // one A operand block
 };
 
-// token of score tile T, column j
-template <int G>
-__device__ __forceinline__ int gx_token(int T, int j) {
-  constexpr int NTB = Gx<G>::NTB;
-  return 128 * (T / NTB) + mx_item(NTB * j + T % NTB);
+// token of score tile T, column j (j < 16)
+__device__ __forceinline__ int gx_token(int T, int j) { return 16 * T + mx_item(j); }
+
+// 4 x 4 byte transpose in each quad of lanes: byte b of lane 4m + i's result
+// is byte i of lane 4m + b's x. Two exchanges: 16-bit halves with lane i ^ 2,
+// then bytes with lane i ^ 1 (v_perm_b32 picks bytes 0-3 from its second
+// operand and 4-7 from its first).
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, int lane) {
+  const int i = lane & 3;
+  const uint32_t p = uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kQuadSwap2, 0xF, 0xF, false));
+  const uint32_t e = __builtin_amdgcn_perm(p, x, (i & 2) ? 0x03020706u : 0x05040100u);
+  const uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(e), kQuadSwap1, 0xF, 0xF, false));
+  return __builtin_amdgcn_perm(o, e, (i & 1) ? 0x03070105u : 0x06020400u);
 }
 
 // The part of a page one lane reads from memory.
@@ -64,9 +74,9 @@ __device__ __forceinline__ void gx_load(GxPage<G>& r, const uint8_t* __restrict_
   r.km[0] = ld_nt4(pg + kmeta_off(G) + 32 * j);
   r.km[1] = ld_nt4(pg + kmeta_off(G) + 32 * j + 16);
 #pragma unroll
-  for (int T = 0; T < NT; ++T) r.kc[T] = ld_nt2(pg + gx_token<G>(T, j) * (D / 4) + 8 * g);
+  for (int T = 0; T < NT; ++T) r.kc[T] = ld_nt2(pg + gx_token(T, j) * (D / 4) + 8 * g);
 #pragma unroll
-  for (int T = 0; T < NT; ++T) r.vm[T] = ld_nt1(pg + vmeta_off(G) + 4 * gx_token<G>(T, j));
+  for (int T = 0; T < NT; ++T) r.vm[T] = ld_nt1(pg + vmeta_off(G) + 4 * gx_token(T, j));
 #pragma unroll
   for (int C = 0; C < 8; ++C)
 #pragma unroll
@@ -209,7 +219,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
   if (n_valid < G) {
 #pragma unroll
     for (int T = 0; T < NT; ++T)
-      if (gx_token<G>(T, j) >= n_valid)
+      if (gx_token(T, j) >= n_valid)
 #pragma unroll
         for (int a = 0; a < NA; ++a) z[a][T] = -INFINITY;
   }
@@ -254,20 +264,21 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
     const int ep = mx_exp(row_max(pmax));
 #pragma unroll
     for (int T = 0; T < NT; ++T) pp[T] = __builtin_amdgcn_ldexpf(pp[T], 4 - ep);
+    // tiles 4u..4u+3 of block h: slots 16(4u + i) + 4(j >> 2) + 0..3 of a
+    // digit row come from lanes 4(j >> 2) + 0..3; lane j writes tile 4u + (j & 3)
 #pragma unroll
     for (int h = 0; h < NB; ++h) {
       uint8_t* blk = L.pa(a, h);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float d[NTB];
 #pragma unroll
-        for (int t = 0; t < NTB; ++t) d[t] = gx_digit(pp[h * NTB + t]);
-        uint8_t* dst = blk + RS * (4 * g + k) + NTB * j;
-        if constexpr (NTB == 8) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack4_fp8(d[0], d[1], d[2], d[3]),
-                                                      pack4_fp8(d[4], d[5], d[6], d[7]));
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pack4_fp8(d[0], d[1], d[2], d[3]);
+        for (int u = 0; u < NTB / 4; ++u) {
+          const int T0 = h * NTB + 4 * u;
+          const float d0 = gx_digit(pp[T0]), d1 = gx_digit(pp[T0 + 1]);
+          const float d2 = gx_digit(pp[T0 + 2]), d3 = gx_digit(pp[T0 + 3]);
+          const uint32_t w = quad_transpose_bytes(pack4_fp8(d0, d1, d2, d3), lane);
+          *reinterpret_cast<uint32_t*>(blk + RS * (4 * g + k) + 16 * (4 * u + (j & 3)) +
+                                       4 * (j >> 2)) = w;
         }
       }
     }
