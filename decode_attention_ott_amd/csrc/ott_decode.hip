@@ -80,7 +80,10 @@ __device__ __forceinline__ int mx_scale(int e, int lane) {
 
 // Lane (j, g) of a page of G tokens: K tiles T = 0..G/16-1 (token 16T + j);
 // the lane's tokens are slots 16g + j + 64i, i < G/64; V k-blocks of 128 slots
-// (G = 64 leaves the upper half of the one block empty).
+// (G = 64 leaves the upper half of the one block empty). At G = 256 block h
+// holds the 32-slot stretches 64g' + 32h + 0..31 (g' = 0..3), so that a lane
+// reads 16 contiguous bytes of a channel's 64-byte code row for both blocks
+// and no cache line is requested by two loads.
 template <int G>
 struct MxPage {
   static constexpr int NT = G / 16;              // K tiles
@@ -88,6 +91,7 @@ struct MxPage {
   static constexpr int NB = (G + 127) / 128;     // V k-blocks
   uint2 kc[NT];     // K tile T: token 16T + j, channel items 32g..32g+31
   uint2 vc[8][NB];  // V tile C, block h: channel 16C + j, slots 128h + 32g + 0..31
+                    // (G = 256: slots 64g + 32h + 0..31)
   uint32_t km[2];   // K (min, scale) of the lane's channels c0 and c0 + 2
   uint32_t vm[NZ];  // V (min, scale) of the lane's slots
 };
@@ -108,8 +112,14 @@ __device__ __forceinline__ void mx_load(MxPage<G>& r, const uint8_t* __restrict_
 #pragma unroll
     for (int h = 0; h < P::NB; ++h) {
       const uint8_t* row = pg + vcode_off(G) + (16 * C + j) * (G / 4);
-      if constexpr (G >= 128) {
-        r.vc[C][h] = ld_nt2(row + 32 * h + 8 * g);
+      if constexpr (G == 256) {
+        if (h == 0) {
+          const uint4 x = ld_nt4(row + 16 * g);
+          r.vc[C][0] = make_uint2(x.x, x.y);
+          r.vc[C][1] = make_uint2(x.z, x.w);
+        }
+      } else if constexpr (G == 128) {
+        r.vc[C][h] = ld_nt2(row + 8 * g);
       } else {  // a 16-byte row: lane groups 2 and 3 have no slots
         r.vc[C][h] = ld_nt2(row + 8 * (g & 1));
         if (g >= 2) r.vc[C][h] = make_uint2(0u, 0u);
@@ -177,19 +187,22 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
   }
   const int ep = mx_exp(wave_max(pmax));
   {
-    const int kt = mx_k(t0);  // slot t0 + 64i sits in block i/2 at kt + 64 (i & 1)
+    // slot t0 + 64i sits in block i/2 at mx_k(t0) + 64 (i & 1); at G = 256 in
+    // block t0 / 32 at mx_k(t0 % 32) + 32i
+    constexpr int kStep = G == 256 ? 32 : 64;
 #pragma unroll
     for (int i = 0; i < NZ; i += 2) {
       float d0[4], d1[4];
       mx_digits(pp[i], ep, d0);
       if (i + 1 < NZ) mx_digits(pp[i + 1], ep, d1);
-      uint8_t* blk = pa + 512 * (i / 2) + kt;
+      uint8_t* blk = G == 256 ? pa + 512 * (t0 >> 5) + mx_k(t0 & 31) + 32 * i
+                              : pa + 512 * (i / 2) + mx_k(t0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t w = uint32_t(
             __builtin_amdgcn_cvt_pk_fp8_f32(d0[k], i + 1 < NZ ? d1[k] : 0.f, 0, false));
         blk[128 * k] = uint8_t(w);
-        if (i + 1 < NZ) blk[128 * k + 64] = uint8_t(w >> 8);
+        if (i + 1 < NZ) blk[128 * k + kStep] = uint8_t(w >> 8);
       }
     }
   }

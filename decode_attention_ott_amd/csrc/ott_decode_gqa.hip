@@ -64,7 +64,8 @@ struct GxPage {
   uint4 km[2];         // K (min, scale) of channels 8(lane&15)..+7
   uint2 kc[NT];        // K codes: tile T, token gx_token(T, lane&15), channels 32g..32g+31
   uint32_t vm[NT];     // V (min, scale) of the lane's tokens
-  uint2 vc[8][NB];     // V codes: channel 16C + (lane&15), slots 128h + 32g..+31
+  uint2 vc[8][NB];     // V codes: channel 16C + (lane&15), block h: slots 128h + 32g..+31
+                       // (G = 256: slots 64g + 32h..+31, one 16-byte load for both)
 };
 
 template <int G>
@@ -82,8 +83,14 @@ __device__ __forceinline__ void gx_load(GxPage<G>& r, const uint8_t* __restrict_
 #pragma unroll
     for (int h = 0; h < NB; ++h) {
       const uint8_t* row = pg + vcode_off(G) + (16 * C + j) * (G / 4);
-      if constexpr (G >= 128) {
-        r.vc[C][h] = ld_nt2(row + 32 * h + 8 * g);
+      if constexpr (G == 256) {
+        if (h == 0) {
+          const uint4 x = ld_nt4(row + 16 * g);
+          r.vc[C][0] = make_uint2(x.x, x.y);
+          r.vc[C][1] = make_uint2(x.z, x.w);
+        }
+      } else if constexpr (G == 128) {
+        r.vc[C][h] = ld_nt2(row + 8 * g);
       } else {  // a 16-byte row: lane groups 2 and 3 have no slots
         r.vc[C][h] = ld_nt2(row + 8 * (g & 1));
         if (g >= 2) r.vc[C][h] = make_uint2(0u, 0u);
@@ -264,22 +271,22 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
     const int ep = mx_exp(row_max(pmax));
 #pragma unroll
     for (int T = 0; T < NT; ++T) pp[T] = __builtin_amdgcn_ldexpf(pp[T], 4 - ep);
-    // tiles 4u..4u+3 of block h: slots 16(4u + i) + 4(j >> 2) + 0..3 of a
-    // digit row come from lanes 4(j >> 2) + 0..3; lane j writes tile 4u + (j & 3)
+    // tiles 4u..4u+3: slots 4(j >> 2) + 0..3 of tile T's 16-slot stretch of a
+    // digit row come from lanes 4(j >> 2) + 0..3; lane j writes tile
+    // T = 4u + (j & 3). The stretch is 16T of block 0 (G <= 128); at G = 256,
+    // 32(T / 4) + 16(T % 2) of block (T / 2) % 2.
+    const int tq = j & 3;
 #pragma unroll
-    for (int h = 0; h < NB; ++h) {
-      uint8_t* blk = L.pa(a, h);
+    for (int k = 0; k < 4; ++k) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int u = 0; u < NTB / 4; ++u) {
-          const int T0 = h * NTB + 4 * u;
-          const float d0 = gx_digit(pp[T0]), d1 = gx_digit(pp[T0 + 1]);
-          const float d2 = gx_digit(pp[T0 + 2]), d3 = gx_digit(pp[T0 + 3]);
-          const uint32_t w = quad_transpose_bytes(pack4_fp8(d0, d1, d2, d3), lane);
-          *reinterpret_cast<uint32_t*>(blk + RS * (4 * g + k) + 16 * (4 * u + (j & 3)) +
-                                       4 * (j >> 2)) = w;
-        }
+      for (int u = 0; u < NT / 4; ++u) {
+        const int T0 = 4 * u;
+        const float d0 = gx_digit(pp[T0]), d1 = gx_digit(pp[T0 + 1]);
+        const float d2 = gx_digit(pp[T0 + 2]), d3 = gx_digit(pp[T0 + 3]);
+        const uint32_t w = quad_transpose_bytes(pack4_fp8(d0, d1, d2, d3), lane);
+        uint8_t* blk = G == 256 ? L.pa(a, tq >> 1) + 32 * u + 16 * (tq & 1)
+                                : L.pa(a, 0) + 16 * (4 * u + tq);
+        *reinterpret_cast<uint32_t*>(blk + RS * (4 * g + k) + 4 * (j >> 2)) = w;
       }
     }
     sp[a] = gx_scale(ep, lane);
