@@ -31,6 +31,9 @@ constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// the kernels move fp16 rows in 16-byte pieces
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 ott_status_t validate_config(const ott_config_t* c) {
   if (!c) return OTT_ERR_INVALID_ARG;
   if (c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1 || c->max_seq_len < 1 ||
@@ -200,7 +203,7 @@ ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const 
     if (n > 0) any = true;
   }
   if (!any) return OTT_OK;
-  if (!d_k || !d_v) return OTT_ERR_INVALID_ARG;
+  if (!d_k || !d_v || misaligned16(d_k) || misaligned16(d_v)) return OTT_ERR_INVALID_ARG;
   for (int b = 0; b < B; ++b) {
     const int n = h_n_new[b];
     if (h->rcnt[b] + n > C) return OTT_ERR_CAPACITY;
@@ -262,8 +265,7 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
     any |= h_len[b] > 0;
   }
   if (!any) return OTT_OK;
-  if (!d_k || !d_v || (reinterpret_cast<uintptr_t>(d_k) & 15) || (reinterpret_cast<uintptr_t>(d_v) & 15))
-    return OTT_ERR_INVALID_ARG;
+  if (!d_k || !d_v || misaligned16(d_k) || misaligned16(d_v)) return OTT_ERR_INVALID_ARG;
   int max_pages = 0;
   for (int b = 0; b < B; ++b)
     if (h_len[b] >= R + G) max_pages = std::max(max_pages, (h_len[b] - R) / G);
@@ -284,7 +286,7 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
 ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream) {
   ott_status_t st = check_handle(h);
   if (st != OTT_OK) return st;
-  if (!d_q || !d_out) return OTT_ERR_INVALID_ARG;
+  if (!d_q || !d_out || misaligned16(d_q) || misaligned16(d_out)) return OTT_ERR_INVALID_ARG;
   const int B = h->cfg.batch;
   // bytes of the largest head (pages + fp16 tokens) bound the useful split count
   int64_t bytes_max = 0;
@@ -310,7 +312,8 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
   ord.n = 0;
   const int Hkv = h->cfg.num_kv_heads;
   const int64_t heads = int64_t(B) * Hkv;
-  if (S == 1 && heads <= ott::kMaxOrdered && heads > h->cus) {
+  // (only whole rounds: a partial last round would leave holes in the order)
+  if (S == 1 && heads <= ott::kMaxOrdered && heads > h->cus && heads % h->cus == 0) {
     std::vector<int32_t>& seq = h->seq_by_size;
     seq.resize(B);
     for (int b = 0; b < B; ++b) seq[b] = b;
@@ -328,8 +331,7 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
         ord.bh[slot] = uint16_t(b * Hkv + hh);
       }
     }
-    // a partial last round leaves holes: fall back to the identity
-    ord.n = (heads % C == 0) ? int32_t(heads) : 0;
+    ord.n = int32_t(heads);
   }
   return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, ord,
                                             static_cast<hipStream_t>(stream)));
@@ -403,8 +405,7 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
     return OTT_ERR_INVALID_ARG;
   if (head_dim != ott::kHeadDim) return OTT_ERR_UNSUPPORTED;
   if (!d_k || !d_v || !d_q || !d_out) return OTT_ERR_INVALID_ARG;
-  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(d_k) || misaligned(d_v) || misaligned(d_q) || misaligned(d_out))
+  if (misaligned16(d_k) || misaligned16(d_v) || misaligned16(d_q) || misaligned16(d_out))
     return OTT_ERR_INVALID_ARG;
   ott::Fp16Lens lens;
   int32_t lmax = 0;

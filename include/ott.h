@@ -144,8 +144,9 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
 /*
  * ott_append - add new tokens to each sequence's fp16 window ([Blog] 3.3: the
  * residual window keeps recent tokens in FP16).
- *   d_k, d_v : device fp16 [B][Hkv][max_new][d]; token i of sequence b is row i
- *              and takes position L_b + i. Copied; reusable once the stream has run.
+ *   d_k, d_v : device fp16 [B][Hkv][max_new][d], 16-byte aligned; token i of
+ *              sequence b is row i and takes position L_b + i. Copied; reusable once
+ *              the stream has run. NULL or misaligned: OTT_ERR_INVALID_ARG.
  *   h_n_new  : host int32 [B], 0 <= n_new[b] <= max_new.
  *   Fails with OTT_ERR_CAPACITY (nothing enqueued) when some r_cnt_b + n_new[b]
  *   exceeds R+G (call ott_quantize_group first) or L_b + n_new[b] > max_seq_len.
@@ -192,7 +193,8 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
  *   out = sum_i softmax_i(sm_scale * q.k_i) v_i over every cached token of b:
  *   dequantized page tokens (k = min + scale*code), the fp16 pool and the fp16
  *   window, with one softmax over all of them.
- *   d_q   : device fp16 [B][Hq][d];  d_out : device fp16 [B][Hq][d].
+ *   d_q   : device fp16 [B][Hq][d];  d_out : device fp16 [B][Hq][d]; both 16-byte
+ *           aligned (else OTT_ERR_INVALID_ARG).
  *   The state is not modified; the call can be repeated.
  *   OTT_ERR_STATE if some sequence holds no token.
  */

@@ -130,6 +130,31 @@ def test_capacity_error_leaves_state_unchanged():
     assert layer.seq_state(0) == (161, 33, 128, 1)
 
 
+def test_misaligned_rows_are_rejected_before_any_launch():
+    """The kernels move fp16 rows in 16-byte pieces: inputs and outputs off a
+    16-byte boundary are refused (OTT_ERR_INVALID_ARG) and leave the state as it was."""
+    import torch
+    from decode_attention_ott_amd import OTTLayer, OttError
+    from decode_attention_ott_amd import _lib as L
+    layer = OTTLayer(1, 2, 1, 128, 128, 32, 32, max_seq_len=400)
+    buf = torch.zeros(2 * 8 * 128 + 8, dtype=torch.float16, device="cuda")
+    k = buf[:8 * 128].view(1, 1, 8, 128)
+    off = buf[1:1 + 8 * 128]  # 2 bytes past a 16-byte boundary
+    assert off.data_ptr() % 16 == 2
+    with pytest.raises(OttError, match="INVALID_ARG"):
+        L.ott_append(layer.handle, off.data_ptr(), k.data_ptr(), [8], 8, 0)
+    assert layer.seq_state(0) == (0, 0, 0, 0)
+    layer.append(k, k)
+    q = torch.zeros(1, 2, 128, dtype=torch.float16, device="cuda")
+    out = torch.zeros(2 * 128 + 8, dtype=torch.float16, device="cuda")
+    with pytest.raises(OttError, match="INVALID_ARG"):
+        L.ott_decode(layer.handle, q.data_ptr(), out[1:].data_ptr(), 0)
+    with pytest.raises(OttError, match="INVALID_ARG"):
+        L.ott_decode(layer.handle, off.data_ptr(), out.data_ptr(), 0)
+    torch.cuda.synchronize()
+    assert layer.seq_state(0) == (8, 8, 0, 0)
+
+
 @pytest.mark.parametrize("rule", [1, 2])
 @pytest.mark.parametrize("G,R,P,Hq,steps", [(128, 32, 32, 2, 4), (64, 16, 8, 8, 70)])
 def test_other_retention_rules(rule, G, R, P, Hq, steps):
