@@ -83,6 +83,16 @@ def test_ragged_and_short_sequences():
     run_case(w, lengths=[1, 50, 159, 200, 777], state_every_step=True)
 
 
+def test_one_split_head_orders():
+    """One split per head with more heads than CUs: 512 heads of ragged lengths
+    (a whole number of rounds: the heads are dealt largest first, snaking) and
+    300 heads (a partial last round: the launch keeps the identity order)."""
+    for B, H in ((16, 32), (10, 30)):
+        w = small(f"order{B}x{H}", B=B, Hq=H, Hkv=H, L=(300, 700), steps=3, seed=5)
+        heads = [(b, (7 * b) % H) for b in range(B)]
+        run_case(w, heads=heads, splits=[1], check_prefill=False)
+
+
 def test_split_counts_agree():
     w = small("splits", B=2, Hq=2, Hkv=2, L=(2000, 2000), steps=3)
     run_case(w, splits=[1, 2, 3, 7, 16, 0])
