@@ -19,12 +19,12 @@
 // head of the group: its scores, its softmax state and its value sums.
 //
 // Token order of the score tiles. K tile T holds the 16 consecutive tokens
-// 16T..16T+15, column j the one at logical slot 16T + j of the value operand
-// (token 16T + mx_item(j)), so each load of a tile's codes reads whole cache
-// lines that no other load of the page touches. A lane's scores then sit at
-// one slot in each 16-slot stretch; a 4 x 4 byte transpose inside each quad of
-// lanes turns every 4 tiles of a digit row of p' into one 4-byte LDS write per
-// lane.
+// 16T..16T+15; column j is token 16T + mx_item(j), the one at position j of
+// the tile's 16-slot stretch of the value operand. So each load of a tile's
+// codes reads whole cache lines that no other load of the page touches. A
+// lane's scores then sit at one slot in each 16-slot stretch; a 4 x 4 byte
+// transpose inside each quad of lanes turns every 4 tiles of a digit row of p'
+// into one 4-byte LDS write per lane.
 #include "ott_decode_common.h"
 #include "ott_mx.h"
 
@@ -36,7 +36,6 @@ using namespace dec;
 template <int G>
 struct Gx {
   static constexpr int NB = (G + 127) / 128;         // value k-blocks of 128 slots
-  static constexpr int NTB = G >= 128 ? 8 : G / 16;  // score tiles per block
   static constexpr int NT = G / 16;                  // score tiles
   static constexpr int RS = 144;                     // LDS bytes per A row (128 + pad)
   static constexpr int ABLK = 16 * RS;               // one A operand block
@@ -158,7 +157,7 @@ struct alignas(16) GxLds {
 template <int G, int NA>
 __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const float (&qs)[NA][8],
                                         GxLds<G, NA>& L, GxState<NA>& st, int lane) {
-  constexpr int NT = Gx<G>::NT, NB = Gx<G>::NB, NTB = Gx<G>::NTB, RS = Gx<G>::RS;
+  constexpr int NT = Gx<G>::NT, NB = Gx<G>::NB, RS = Gx<G>::RS;
   const int j = lane & 15, g = lane >> 4;
 
   // ---- q' = qs scale_c for head g of each group, channels 8j..8j+7, as digits
