@@ -100,6 +100,13 @@ def test_prefill_matches_stepwise(G, R, P, lengths):
     _compare(small(f"prefill-g{G}r{R}p{P}", G=G, R=R, P=P, seed=G + R + P), lengths)
 
 
+@pytest.mark.parametrize("rule", [1, 2])
+def test_prefill_matches_stepwise_other_retention_rules(rule):
+    """Largest-norm and random retention: the one-call prefill walks the groups
+    with the same rule as the stepwise quantize steps."""
+    _compare(small(f"prefill-rule{rule}", retention=rule, seed=40 + rule), [1000, 417, 288, 161])
+
+
 def test_prefill_with_pool_churn():
     _compare(small("prefill-churn", tok_prob=0.05, chan_scale=30.0), [1500, 1400, 900, 1501])
 
