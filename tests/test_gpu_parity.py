@@ -98,6 +98,15 @@ def test_split_counts_agree():
     run_case(w, splits=[1, 2, 3, 7, 16, 0])
 
 
+@pytest.mark.parametrize("Hq", [2, 8])
+def test_split_counts_agree_at_g256(Hq):
+    """G = 256 (value blocks as interleaved 32-slot stretches) on the one-head
+    and the grouped-query kernel, with 1 to 16 splits over a head's pages."""
+    w = small(f"splits-g256-h{Hq}", B=2, Hq=Hq, Hkv=2, G=256, R=64, P=32, L=(3000, 3000), steps=2,
+              seed=29)
+    run_case(w, splits=[1, 2, 5, 16, 0])
+
+
 def test_large_scores_are_safe():
     """Queries scaled x16: scores in the hundreds; the online softmax must
     rescale without overflow (softmax shift invariance)."""
