@@ -37,7 +37,8 @@ Readings taken where the pages are silent:
   R5  quantize when the window holds >= R+G tokens, taking the oldest G.
   R6  asymmetric uniform 2-bit quantizer: x_hat = min + code * scale,
       scale = (max - min) / 3, levels 0..3.
-  R7  min and scale stored as fp16; scale = fp16_rne(fp32(max - min) / 3).
+  R7  min and scale stored as fp16; scale = fp16_rne(fp32(max - min) / 3);
+      a zero min or scale is stored as +0.
   R8  code = clamp(rint_half_even(fp32((x - min)) / fp32(scale)), 0, 3), one IEEE
       fp32 op per step; scale == 0 gives code 0.
   R9  prefill is appends plus quantize steps in position order.
@@ -48,9 +49,11 @@ Readings taken where the pages are silent:
   R16 the comparison rules of [Abs] Fig. 1(c), built for the accuracy measurement:
       largest squared norm, or a random key per position (SplitMix64).
 
-What pins this module (tests/test_oracle.py): hand-derived quantizer cases,
-the quantizer's error bound and nearest-level brute force, fp16 rounding
-against Python's struct, brute-force top-P pool membership for every rule,
+What pins this module (tests/test_oracle.py): hand-derived quantizer cases
+(signed zeros included), the quantizer's error bound and nearest-level brute
+force, fp16 rounding against Python's struct, hand-derived squared norms whose
+fp64 value depends on the summation order (and the pool tie they decide),
+brute-force top-P pool membership for every rule,
 the SplitMix64 reference outputs, token accounting, and reductions of the
 decode to textbook attention (no quantization, lossless grids, permutation
 and shift invariance, closed forms). Parity with the paper's own arithmetic
@@ -92,7 +95,10 @@ def min_scale(values_f16: np.ndarray) -> Tuple[np.float16, np.float16]:
     """(min, scale) of one quantization set, as fp16 (readings R6, R7).
 
     scale = fp16_rne( (fp32(max) - fp32(min)) / 3.0f ), each step one IEEE op.
-    An empty set gives (0, 0).
+    A zero min or scale is stored as +0 whatever the signs of the zeros in the
+    set (reading R7: a set may hold +0 and -0, which compare equal, so "the
+    minimum" names no single bit pattern; dequantized values do not depend on
+    the choice). An empty set gives (+0, +0).
     """
     v = np.asarray(values_f16, dtype=F16)
     if v.size == 0:
@@ -101,6 +107,10 @@ def min_scale(values_f16: np.ndarray) -> Tuple[np.float16, np.float16]:
     hi = v.max()
     r = F32(hi) - F32(lo)
     s = F16(r / F32(3.0))
+    if lo == 0:
+        lo = F16(0.0)
+    if s == 0:
+        s = F16(0.0)
     return F16(lo), s
 
 
@@ -232,6 +242,10 @@ class HeadOracle:
         self.pool: List[Entry] = []          # ascending (key, pos)
         self.recent: List[Entry] = []        # ascending pos
         self.L = 0
+        # pages' positions, K_hat and V_hat concatenated, rebuilt when a page is
+        # added (pages never change once made); a cache only, no arithmetic
+        self._pages_cat = None
+        self._pages_cat_n = None
 
     # -- stage: append (every step) -------------------------------------
     def append(self, k_rows: np.ndarray, v_rows: np.ndarray) -> None:
@@ -282,12 +296,16 @@ class HeadOracle:
         Order: quantized pages, outlier pool, residual window ([Blog] 3.3).
         """
         d = self.d
-        if self.pages:
-            qpos = np.concatenate([p.pos for p in self.pages])
-            qk = np.concatenate([p.k_hat() for p in self.pages])
-            qv = np.concatenate([p.v_hat() for p in self.pages])
-        else:
-            qpos, qk, qv = np.zeros(0, np.int64), np.zeros((0, d)), np.zeros((0, d))
+        tag = (len(self.pages), id(self.pages[-1]) if self.pages else 0)
+        if self._pages_cat_n != tag:
+            if self.pages:
+                self._pages_cat = (np.concatenate([p.pos for p in self.pages]),
+                                   np.concatenate([p.k_hat() for p in self.pages]),
+                                   np.concatenate([p.v_hat() for p in self.pages]))
+            else:
+                self._pages_cat = (np.zeros(0, np.int64), np.zeros((0, d)), np.zeros((0, d)))
+            self._pages_cat_n = tag
+        qpos, qk, qv = self._pages_cat
 
         def dense(entries):
             if not entries:

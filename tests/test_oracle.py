@@ -145,6 +145,75 @@ def _exact_sq_norm(row) -> Fraction:
     return sum(Fraction(float(x)) ** 2 for x in row)
 
 
+def _order_rows(d=128):
+    """Row A = [8, 2^-24 x (d-1)] and row B = A reversed (fp16)."""
+    a = np.full(d, 2.0 ** -24, np.float16)
+    a[0] = 8
+    return a, a[::-1].copy()
+
+
+def test_squared_norm_runs_in_channel_order():
+    """Reading R2: the squared Key norm is an fp64 sum taken channel 0, 1, ...,
+    d-1. Row A = [8, 2^-24, ..., 2^-24]: 8^2 = 64 comes first, and each 2^-48
+    that follows is a quarter of the fp64 spacing at 64 (2^-46), so every partial
+    sum rounds back to 64: the norm is exactly 64. Row B is A reversed: the 127
+    squares 2^-48 add up exactly to 127 * 2^-48 = 31.75 * 2^-46 first, and
+    64 + 31.75 * 2^-46 rounds to 64 + 32 * 2^-46 = 64 + 2^-41. A pairwise, dot
+    or reversed summation gives other values for A."""
+    a, b = _order_rows()
+    n2 = O.sq_key_norm(np.stack([a, b]))
+    assert n2[0] == 64.0
+    assert n2[1] == 64.0 + 2.0 ** -41
+
+
+def test_norm_order_decides_pool_ties():
+    """The same rows through a quantize step (G = 4, R = 0, P = 1): row C =
+    [8, 0, ..., 0] has norm exactly 64. A (position 0) ties with C (position 1),
+    so the lower position keeps the pool slot; B (position 0) is larger than C
+    by 2^-41, so C keeps it."""
+    a, b = _order_rows()
+    c = np.zeros(128, np.float16)
+    c[0] = 8
+    filler = np.full(128, 4.0, np.float16)      # norm 2048: never in the pool
+    v = np.zeros((4, 128), np.float16)
+    for first, want in ((a, [0]), (b, [1])):
+        st = O.HeadOracle(128, 4, 0, 1)
+        st.append(np.stack([first, c, filler, filler]), v)
+        st.quantize_group()
+        assert [e.pos for e in st.pool] == want
+
+
+def test_signed_zero_page_metadata():
+    """Reading R7 on a whole page: a Key channel whose minimum is zero, with +0
+    and -0 both among the members, and a Value row holding both zeros at its
+    minimum, store +0 as their min whatever order the members come in.
+    Channel 0 holds {-0, +0, 3, 1.5} -> min +0, scale 1 (r = 3); Value row 0 is
+    {+0, -0, 3, 0, ...} -> min +0, scale 1; Value row 1 is all -0 -> min +0,
+    scale +0. Hand-derived from the definition (no oracle call builds them)."""
+    d, G = 8, 4
+    k = np.zeros((4, d), np.float16)
+    k[:, 0] = np.float16([-0.0, 0.0, 3.0, 1.5])
+    k[:, 1:] = 1.0
+    v = np.zeros((4, d), np.float16)
+    v[0, :3] = np.float16([0.0, -0.0, 3.0])
+    v[1, :] = np.float16(-0.0)
+    v[2:, :] = 1.0
+    for order in ([0, 1, 2, 3], [1, 0, 3, 2]):
+        kk = k[order]
+        vv = v[order]
+        pg = O.quantize_members(kk, vv, np.arange(4))
+        b = O.pack_page(pg, G, d)
+        moff = 2 * (G * d // 4)
+        km = np.frombuffer(b[moff:moff + 4 * d], "<u2").reshape(d, 2)
+        vm = np.frombuffer(b[moff + 4 * d:], "<u2").reshape(G, 2)
+        assert km[0].tolist() == [0x0000, 0x3C00]            # +0, 1.0
+        r0, r1 = order.index(0), order.index(1)
+        assert vm[r0].tolist() == [0x0000, 0x3C00]
+        assert vm[r1].tolist() == [0x0000, 0x0000]
+        # channel 0 codes: -0 -> 0, +0 -> 0, 3 -> 3, 1.5 -> half-even 2
+        assert pg.k_code[:, 0].tolist() == [[0, 0, 3, 2][i] for i in order]
+
+
 @pytest.mark.parametrize("G", [2, 4, 8])
 @pytest.mark.parametrize("P", [0, 1, 3, "G", "2G"])
 @pytest.mark.parametrize("d", [4, 8])
@@ -480,3 +549,42 @@ def test_planted_transposed_kv_is_caught(monkeypatch):
     monkeypatch.setattr(O.HeadOracle, "caches", swapped)
     with pytest.raises(AssertionError):
         test_decode_without_quantization_is_attention()
+
+
+def test_planted_pairwise_norm_is_caught(monkeypatch):
+    """A squared norm summed pairwise (numpy's np.sum) instead of in channel order
+    must break the R2 pins."""
+    monkeypatch.setattr(O, "sq_key_norm", lambda rows: np.sum(
+        np.atleast_2d(np.asarray(rows, np.float16)).astype(np.float64) ** 2, axis=1))
+    with pytest.raises(AssertionError):
+        test_squared_norm_runs_in_channel_order()
+    with pytest.raises(AssertionError):
+        test_norm_order_decides_pool_ties()
+
+
+def test_planted_reversed_norm_is_caught(monkeypatch):
+    def rev(rows):
+        x = np.atleast_2d(np.asarray(rows, np.float16)).astype(np.float64)
+        acc = np.zeros(x.shape[0])
+        for c in range(x.shape[1] - 1, -1, -1):
+            acc = acc + x[:, c] * x[:, c]
+        return acc
+    monkeypatch.setattr(O, "sq_key_norm", rev)
+    with pytest.raises(AssertionError):
+        test_squared_norm_runs_in_channel_order()
+
+
+def test_planted_signed_zero_min_is_caught(monkeypatch):
+    """Storing the minimum with the sign of whichever zero the scan meets first
+    (numpy's min) must break the signed-zero pins."""
+    def raw_min_scale(values):
+        v = np.asarray(values, np.float16)
+        if v.size == 0:
+            return np.float16(0), np.float16(0)
+        lo, hi = v.min(), v.max()
+        return np.float16(lo), np.float16((np.float32(hi) - np.float32(lo)) / np.float32(3))
+    monkeypatch.setattr(O, "min_scale", raw_min_scale)
+    with pytest.raises(AssertionError):
+        test_quantizer_hand_cases()
+    with pytest.raises(AssertionError):
+        test_signed_zero_page_metadata()
