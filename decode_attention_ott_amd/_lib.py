@@ -43,7 +43,7 @@ class ott_layout_t(ctypes.Structure):
                 ("off_pool_k", ctypes.c_uint64), ("off_pool_v", ctypes.c_uint64),
                 ("off_pool_pos", ctypes.c_uint64), ("off_pool_n2", ctypes.c_uint64),
                 ("off_ring_k", ctypes.c_uint64), ("off_ring_v", ctypes.c_uint64),
-                ("off_partials", ctypes.c_uint64), ("off_split_sync", ctypes.c_uint64)]
+                ("off_partials", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -99,6 +99,19 @@ def _check(status: int, where: str) -> None:
         raise OttError(status, where)
 
 
+# Batch size of each live handle: ott_append and ott_prefill read exactly that
+# many host counts, so a list of another length is refused before the call.
+_batch_of = {}
+
+
+def _host_counts(h, values, what: str):
+    n = len(values)
+    want = _batch_of.get(getattr(h, "value", h))
+    if want is not None and n != want:
+        raise ValueError(f"{what} has {n} entries; the handle's batch is {want}")
+    return (ctypes.c_int32 * n)(*[int(x) for x in values])
+
+
 # --- the C calls under their own names --------------------------------------
 
 def ott_init(cfg: ott_config_t, d_arena: Optional[int], arena_bytes: int,
@@ -111,11 +124,12 @@ def ott_init(cfg: ott_config_t, d_arena: Optional[int], arena_bytes: int,
     h = ctypes.c_void_p(0)
     _check(lib.ott_init(ctypes.byref(cfg), ctypes.c_void_p(d_arena), arena_bytes,
                         ctypes.byref(req), ctypes.byref(h)), "ott_init")
+    _batch_of[h.value] = int(cfg.batch)
     return h, int(req.value)
 
 
 def ott_append(h, d_k: int, d_v: int, n_new, max_new: int, stream: int) -> None:
-    arr = (ctypes.c_int32 * len(n_new))(*[int(x) for x in n_new])
+    arr = _host_counts(h, n_new, "n_new")
     _check(lib.ott_append(h, ctypes.c_void_p(d_k), ctypes.c_void_p(d_v), arr, max_new,
                           ctypes.c_void_p(stream)), "ott_append")
 
@@ -128,7 +142,7 @@ def ott_quantize_group(h, stream: int) -> int:
 
 
 def ott_prefill(h, d_k: int, d_v: int, lens, max_len: int, stream: int) -> None:
-    arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+    arr = _host_counts(h, lens, "lens")
     _check(lib.ott_prefill(h, ctypes.c_void_p(d_k), ctypes.c_void_p(d_v), arr, max_len,
                            ctypes.c_void_p(stream)), "ott_prefill")
 
@@ -139,6 +153,7 @@ def ott_decode(h, d_q: int, d_out: int, stream: int) -> None:
 
 
 def ott_destroy(h) -> None:
+    _batch_of.pop(getattr(h, "value", h), None)
     lib.ott_destroy(h)
 
 
@@ -165,6 +180,8 @@ def ott_status_string(status: int) -> str:
 def ott_fp16_decode(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, d_k: int,
                     d_v: int, max_len: int, lens, d_q: int, d_out: int, sm_scale: float,
                     d_work: Optional[int], work_bytes: int, num_splits: int, stream: int) -> None:
+    if len(lens) != batch:
+        raise ValueError(f"lens has {len(lens)} entries; batch is {batch}")
     arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
     _check(lib.ott_fp16_decode(batch, num_q_heads, num_kv_heads, head_dim, ctypes.c_void_p(d_k),
                                ctypes.c_void_p(d_v), max_len, arr, ctypes.c_void_p(d_q),

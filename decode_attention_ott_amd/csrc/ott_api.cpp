@@ -22,6 +22,7 @@ struct ott_ctx {
   ott::HeadOrder order{};  // rebuilt at every one-split decode
   ott::QuantizeList due{};  // rebuilt at every quantize call
   std::vector<int32_t> seq_by_size;
+  bool counters_written = false;  // has a launch on this handle set every head's counters?
   bool poisoned = false;
 };
 
@@ -90,7 +91,6 @@ void fill_layout(const ott_config_t* c, ott_layout_t* L) {
   L->off_ring_k = take(BH * C * d * 2);
   L->off_ring_v = take(BH * C * d * 2);
   L->off_partials = take(B * Hq * uint64_t(L->max_splits) * (2 + d) * sizeof(float));
-  L->off_split_sync = take(B * Hq * sizeof(int32_t));
   L->arena_bytes = off;
 }
 
@@ -157,7 +157,6 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   a.off_ring_k = lay.off_ring_k;
   a.off_ring_v = lay.off_ring_v;
   a.off_partials = lay.off_partials;
-  a.off_split_sync = lay.off_split_sync;
   a.sm_scale = h->cfg.sm_scale;
   a.retention = h->cfg.retention;
   const size_t nb = size_t(cfg->batch);
@@ -165,8 +164,6 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   h->rcnt.assign(nb, 0);
   h->head.assign(nb, 0);
   h->nb.assign(nb, 0);
-  const size_t ctr_bytes = size_t(cfg->batch) * cfg->num_kv_heads * 4 * sizeof(int32_t);
-  const size_t sync_bytes = size_t(cfg->batch) * cfg->num_q_heads * sizeof(int32_t);
   {
     // one round of decode work-groups fills the GPU: CUs x work-groups per CU
     int dev = 0, cus = 0;
@@ -179,11 +176,8 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
     h->slots = int64_t(cus) * wpc;
     h->cus = cus;
   }
-  if (hipMemset(a.base + lay.off_counters, 0, ctr_bytes) != hipSuccess ||
-      hipMemset(a.base + lay.off_split_sync, 0, sync_bytes) != hipSuccess) {
-    delete h;
-    return OTT_ERR_HIP;
-  }
+  // Nothing is written to the arena here: the first ott_append or ott_prefill
+  // launch sets every head's counters on the caller's stream.
   *out = h;
   return OTT_OK;
 }
@@ -212,12 +206,14 @@ ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const 
   ott::AppendCounts cnt{};
   cnt.max_new = max_new;
   cnt.uniform = uniform ? h_n_new[0] : -1;
+  cnt.init = h->counters_written ? 0 : 1;
   for (int b = 0; b < B; ++b) {
     cnt.n[b] = uint16_t(h_n_new[b]);
     cnt.slot0[b] = uint16_t((h->head[b] + h->rcnt[b]) % C);
   }
   st = after_launch(h, ott::launch_append(h->dev, d_k, d_v, cnt, static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
+  h->counters_written = true;
   for (int b = 0; b < B; ++b) {
     h->L[b] += h_n_new[b];
     h->rcnt[b] += h_n_new[b];
@@ -272,6 +268,7 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
   st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens, max_pages,
                                            static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
+  h->counters_written = true;  // the pool walk sets every head's counters, empty ones included
   for (int b = 0; b < B; ++b) {
     const int L = h_len[b];
     const int nq = L >= R + G ? (L - R) / G : 0;

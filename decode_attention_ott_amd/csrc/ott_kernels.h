@@ -9,7 +9,6 @@ namespace ott {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxBatch = 512;
-constexpr int kFp16Chunk = 64;  // window/pool tokens handled per decode work unit
 
 // Device view of one handle's arena. Passed by value to every kernel.
 struct Arena {
@@ -20,7 +19,7 @@ struct Arena {
   uint32_t page_bytes;
   uint64_t off_counters, off_pages, off_page_pos, off_page_nvalid;
   uint64_t off_pool_k, off_pool_v, off_pool_pos, off_pool_n2;
-  uint64_t off_ring_k, off_ring_v, off_partials, off_split_sync;
+  uint64_t off_ring_k, off_ring_v, off_partials;
   float sm_scale;
   int32_t retention;  // pool rule: 0 smallest squared Key norm, 1 largest, 2 random per position
 };
@@ -28,9 +27,13 @@ struct Arena {
 // New-token counts of one ott_append call and the window slot of each
 // sequence's first new token (known to the host, so the kernel's copies do
 // not wait for a counter read); uint16 keeps the kernel argument at 2 KiB.
+// init: the first launch on a handle whose counters no kernel has written yet
+// (the arena's contents are unknown): every head's counters are set to
+// {n, n, 0, 0} instead of being advanced.
 struct AppendCounts {
   int32_t max_new;
   int32_t uniform;  // >= 0: every sequence appends this many; < 0: use n[]
+  int32_t init;
   uint16_t n[kMaxBatch];
   uint16_t slot0[kMaxBatch];
 };

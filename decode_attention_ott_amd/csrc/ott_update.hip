@@ -30,6 +30,13 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
   const int h = blockIdx.x, b = blockIdx.y;
   const int bh = b * a.Hkv + h;
   const int n = cnt.uniform >= 0 ? cnt.uniform : int(cnt.n[b]);
+  if (cnt.init && threadIdx.x == 0) {  // first launch on the handle: counters from scratch
+    int32_t* ctr = counters(a, bh);
+    ctr[0] = n;
+    ctr[1] = n;
+    ctr[2] = 0;
+    ctr[3] = 0;
+  }
   if (n == 0) return;
   uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
   uint4* rv = reinterpret_cast<uint4*>(ring_v(a, bh));
@@ -42,7 +49,7 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
     rk[size_t(slot) * (D / 8) + c] = k[src + i];
     rv[size_t(slot) * (D / 8) + c] = v[src + i];
   }
-  if (threadIdx.x == 0) {  // the only thread touching this head's counters here
+  if (!cnt.init && threadIdx.x == 0) {  // the only thread touching this head's counters here
     int32_t* ctr = counters(a, bh);
     ctr[0] += n;
     ctr[1] += n;
@@ -73,6 +80,14 @@ struct CodeThr {
 __device__ __forceinline__ CodeThr code_thresholds(float m, float s) {
   if (!(s > 0.0f)) return CodeThr{m, INFINITY, INFINITY, INFINITY};
   return CodeThr{m, 0.5f * s, 1.5f * s, 2.5f * s};
+}
+
+// fp16 bits of a stored min or scale: a zero is stored as +0 whichever zero
+// the reduction kept (the set may hold both; they compare equal, so fminf and
+// fmaxf may return either).
+__device__ __forceinline__ uint32_t meta_bits(float x) {
+  const uint32_t h = __half_as_ushort(__float2half_rn(x));
+  return h == 0x8000u ? 0u : h;
 }
 
 __device__ __forceinline__ uint32_t qcode(float x, const CodeThr& q) {
@@ -317,11 +332,12 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
         hi = fmaxf(hi, s.khi[p2 * D + tid]);
       }
       if (n_valid == 0) lo = hi = 0.f;
-      const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
-      s.kq[(tid % 16) * (D / 16) + tid / 16] = code_thresholds(lo, __half2float(sc));
-      const uint32_t word = uint32_t(__half_as_ushort(__float2half_rn(lo))) |
-                            (uint32_t(__half_as_ushort(sc)) << 16);
-      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = word;
+      const uint32_t lo_b = meta_bits(lo);
+      const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
+      s.kq[(tid % 16) * (D / 16) + tid / 16] =
+          code_thresholds(__half2float(__ushort_as_half(uint16_t(lo_b))),
+                          __half2float(__ushort_as_half(uint16_t(sc_b))));
+      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = lo_b | (sc_b << 16);
     }
   }
   __syncthreads();
@@ -383,10 +399,11 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
         mx = fmaxf(mx, __shfl_xor(mx, o));
       }
       if (t < cnt && part == 0) {
-        const __half sc = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
-        s.vq[t0 + t] = code_thresholds(mn, __half2float(sc));
-        vmeta[t0 + t] = uint32_t(__half_as_ushort(__float2half_rn(mn))) |
-                        (uint32_t(__half_as_ushort(sc)) << 16);
+        const uint32_t mn_b = meta_bits(mn);
+        const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+        s.vq[t0 + t] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
+                                       __half2float(__ushort_as_half(uint16_t(sc_b))));
+        vmeta[t0 + t] = mn_b | (sc_b << 16);
       }
     }
     __syncthreads();
@@ -505,7 +522,13 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
   const int h = blockIdx.x, b = blockIdx.y;
   const int bh = b * a.Hkv + h;
   const int L = lens.len[b];
-  if (L == 0) return;
+  if (L == 0) {  // an empty sequence still gets its counters (the arena is not zeroed)
+    if (threadIdx.x == 0) {
+      int32_t* ctr = counters(a, bh);
+      ctr[0] = ctr[1] = ctr[2] = ctr[3] = 0;
+    }
+    return;
+  }
   const int G = a.G, P = a.P, C = a.C;
   const int tid = threadIdx.x;
   const int nq = prefill_pages(a, L);

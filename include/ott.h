@@ -103,10 +103,10 @@ enum { OTT_RETAIN_SMALLEST_NORM = 0, OTT_RETAIN_LARGEST_NORM = 1, OTT_RETAIN_RAN
  *              its first min(P, G*nb) slots are used, ascending (key, position).
  *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
  *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
- *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}.
- *   split_sync int32 [B][Hq]: reserved for arrival counters of an in-kernel split merge;
- *              zeroed by ott_init and not used by the current kernels (a second kernel merges
- *              the splits).
+ *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}
+ *              (written by a split decode, read by the kernel that merges the splits).
+ * No region needs to be cleared by the caller: every byte a kernel reads was
+ * written earlier by one of this handle's kernels.
  */
 typedef struct {
   uint64_t arena_bytes;
@@ -126,16 +126,16 @@ typedef struct {
   uint64_t off_ring_k;
   uint64_t off_ring_v;
   uint64_t off_partials;
-  uint64_t off_split_sync;
 } ott_layout_t;
 
 /*
  * ott_init - validate a config, size the arena, and create a handle.
  *   Sizing: pass d_arena = NULL and out = NULL; *required_bytes receives the size.
  *   Create: pass a device arena of >= required bytes (256-byte aligned); *out
- *   receives the handle. The per-(sequence, head) counters and the split-K
- *   arrival counters are zeroed with blocking hipMemset calls on the default
- *   stream; nothing else is touched.
+ *   receives the handle. The arena may hold anything: ott_init neither reads
+ *   nor writes it and enqueues no work. The first ott_append or ott_prefill
+ *   that launches a kernel sets every (sequence, head) counter on its own
+ *   stream, so the caller's stream order covers the arena from the start.
  *   required_bytes may be NULL when creating.
  */
 ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes,

@@ -73,11 +73,14 @@ def compare_outputs(gpu: np.ndarray, ref: np.ndarray, where: str) -> Tuple[float
 def run_case(w: synth.Workload, steps: Optional[int] = None,
              heads: Optional[Sequence[Tuple[int, int]]] = None,
              lengths: Optional[Sequence[int]] = None, splits: Optional[Sequence[int]] = None,
-             q_scale: float = 1.0, state_every_step: bool = False, check_prefill: bool = True):
+             q_scale: float = 1.0, state_every_step: bool = False, check_prefill: bool = True,
+             plant=None):
     """Prefill + `steps` decode steps on the GPU and in the oracle.
 
     heads: the (sequence, KV head) pairs the oracle follows (default: all).
     splits: split-K factors each decode is run with (default: automatic).
+    plant: optional plant(K, V) that edits the drawn fp16 [B, Hkv, pos, d] inputs
+    in place before either side sees them.
     Returns the worst (max abs, rel L2) seen.
     """
     import torch
@@ -90,6 +93,8 @@ def run_case(w: synth.Workload, steps: Optional[int] = None,
         f" R={w.residual} P={w.pool_size} L={lengths.min()}..{lengths.max()} steps={steps}"
         f" splits={splits} q_scale={q_scale}")
     K, V = synth.kv_all(w, n_pos)
+    if plant is not None:
+        plant(K, V)
     if heads is None:
         heads = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     heads = [(int(b), int(h)) for b, h in heads]

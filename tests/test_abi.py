@@ -53,7 +53,7 @@ def test_sizing_matches_layout_formula():
     want = (al(B * Hkv * 16) + al(B * Hkv * NB * page) + al(B * Hkv * NB * G * 4)
             + al(B * Hkv * NB * 4) + 2 * al(2 * B * Hkv * P * d * 2) + al(2 * B * Hkv * P * 4)
             + al(2 * B * Hkv * P * 8) + 2 * al(B * Hkv * (R + G) * d * 2)
-            + al(B * Hq * S * (2 + d) * 4) + al(B * Hq * 4))
+            + al(B * Hq * S * (2 + d) * 4))
     assert req == want
 
 
@@ -127,3 +127,29 @@ def test_prefill_validates_before_any_gpu_work():
     from decode_attention_ott_amd import _lib as L
     n = (ctypes.c_int32 * 2)(10, 10)
     assert L.lib.ott_prefill(None, None, None, n, 10, None) == 1
+
+
+def test_init_enqueues_nothing_and_host_counts_are_checked():
+    """ott_init neither reads nor writes the arena and enqueues no work: a handle
+    over an arena address that is never dereferenced is created here, where no
+    HIP call could succeed. The binding refuses host count lists whose length is
+    not the handle's batch (the C side reads exactly `batch` entries); a decode
+    of empty sequences and a quantize with no full window enqueue nothing."""
+    from decode_attention_ott_amd import _lib as L
+    cfg = _cfg()
+    need = L.ott_init(cfg, None, 0, sizing_only=True)
+    h, req = L.ott_init(cfg, 1 << 20, need)
+    try:
+        assert req == need
+        with pytest.raises(ValueError, match="batch is 2"):
+            L.ott_append(h, 4096, 4096, [1], 1, 0)
+        with pytest.raises(ValueError, match="batch is 2"):
+            L.ott_prefill(h, 4096, 4096, [5, 5, 5], 5, 0)
+        with pytest.raises(L.OttError, match="STATE"):
+            L.ott_decode(h, 4096, 4096, 0)
+        assert L.ott_quantize_group(h, 0) == 0
+        assert L.ott_get_seq_state(h, 1) == (0, 0, 0, 0)
+        lay = L.ott_get_layout(h)
+        assert lay.arena_bytes == need and lay.off_partials < need
+    finally:
+        L.ott_destroy(h)

@@ -39,6 +39,9 @@ def test_tiny_every_step():
     (128, 0, 32, (400, 400), 12),     # R=0: the window empties at each quantize
     (128, 32, 160, (600, 600), 8),    # P > G: first page empty
     (64, 5, 3, (333, 333), 20),       # odd window and pool sizes
+    (128, 128, 32, (760, 760), 12),   # R=128: window 248 of 256, a quantize at step 7
+    (256, 128, 32, (1146, 1146), 10), # G=256, R=128: window 378 of 384, a quantize at step 5
+    (256, 64, 512, (1082, 1082), 10), # P=512 at G=256: quantize LDS above 64 KiB, a step at 5
 ])
 def test_parameters(G, R, P, L, steps):
     run_case(small(f"g{G}r{R}p{P}", G=G, R=R, P=P, L=L, steps=steps, seed=G + R + P),
@@ -60,6 +63,7 @@ def test_grouped_query_heads(Hq, Hkv):
     (64, 16, 8, (300, 300), 32),      # G=64, 16 heads per pass
     (128, 32, 160, (600, 600), 8),    # P > G: first page has no members
     (128, 32, 0, (500, 500), 4),      # P=0
+    (256, 128, 32, (1146, 1146), 8),  # G=256, R=128
 ])
 def test_grouped_query_parameters(G, R, P, L, Hq):
     run_case(small(f"gqa-g{G}r{R}p{P}h{Hq}", Hq=Hq, G=G, R=R, P=P, L=L, steps=4, seed=3 * G + P),
@@ -105,6 +109,51 @@ def test_split_counts_agree_at_g256(Hq):
     w = small(f"splits-g256-h{Hq}", B=2, Hq=Hq, Hkv=2, G=256, R=64, P=32, L=(3000, 3000), steps=2,
               seed=29)
     run_case(w, splits=[1, 2, 5, 16, 0])
+
+
+def _plant_zeros_and_norm_ties(K, V):
+    """Edits the inputs of a 2-sequence, 2-head case in place.
+    (0, 0): Key channel 5 non-negative with +0 and -0 scattered through it,
+    channel 6 non-negative with -0 as its only zero, channel 7 all zeros of
+    both signs; Value rows non-negative with zeros of both signs, of -0 only,
+    or all zeros of mixed sign (every Key min/scale and Value min/scale rule
+    of the signed-zero reading meets a page).
+    (1, 1): Key rows whose squared norm is 64 in channel order: A = [8, 2^-24,
+    ...] (exactly 64 only in channel order), C = [8, 0, ...] (exactly 64), and
+    B = A reversed (64 + 2^-41), smaller than every drawn token, more of them
+    than the pool holds, so the order of the norm sum decides the pool."""
+    n = K.shape[2]
+    p = np.arange(n)
+    k = K[0, 0]
+    v = V[0, 0]
+    for c in (5, 6):
+        k[:, c] = np.abs(k[:, c])
+    k[p % 37 == 0, 5] = np.float16(-0.0)
+    k[p % 41 == 0, 5] = np.float16(0.0)
+    k[p % 29 == 0, 6] = np.float16(-0.0)
+    k[:, 7] = np.where(p % 2 == 0, np.float16(-0.0), np.float16(0.0))
+    v[:] = np.abs(v)
+    r0, r1, r2 = p % 3 == 0, p % 3 == 1, p % 3 == 2
+    v[r0, 3] = np.float16(-0.0)
+    v[r0, 9] = np.float16(0.0)
+    v[r1, :] = np.where((np.arange(v.shape[1]) % 2 == 0)[None, :], np.float16(-0.0), np.float16(0.0))
+    v[r2, 11] = np.float16(-0.0)
+    a = np.full(K.shape[3], 2.0 ** -24, np.float16)
+    a[0] = 8
+    c = np.zeros(K.shape[3], np.float16)
+    c[0] = 8
+    for base in (256, 650):                 # a prompt group and a group quantized while decoding
+        K[1, 1, base + 2] = a
+        K[1, 1, base + 3] = a[::-1]
+        K[1, 1, base + 4:base + 44] = c
+
+
+def test_signed_zeros_and_norm_order():
+    """Bit-exact pages and pool on inputs where a stored zero min or scale could
+    take either sign, and where only a channel-order fp64 norm sum gives the
+    oracle's pool (the prompt's pages, then a quantize step while decoding)."""
+    w = small("zeros-norms", L=(792, 792), steps=10, seed=77)
+    run_case(w, plant=_plant_zeros_and_norm_ties, state_every_step=True)
 
 
 def test_large_scores_are_safe():
@@ -210,11 +259,15 @@ def test_llama2_7b_b32_sampled():
 
 
 def test_mistral_gqa_sampled():
-    run_case(W["mistral-7b-gqa"], heads=[(0, 0), (3, 5), (7, 7)], steps=6)
+    """Batch 8 at 32K, 4 query heads per KV head, sampled heads: the window
+    goes 128 -> 160, so step 31 quantizes every sequence at full shape."""
+    run_case(W["mistral-7b-gqa"], heads=[(0, 0), (3, 5), (7, 7)], steps=34)
 
 
 def test_llama2_13b_128k_sampled():
-    run_case(W["llama2-13b-128k"], heads=[(0, 0), (0, 23), (0, 39)], steps=6)
+    """128K tokens, G = 256, R = 64, P = 128, sampled heads: the window goes
+    256 -> 320, so step 63 quantizes at full shape (a 512th page)."""
+    run_case(W["llama2-13b-128k"], heads=[(0, 0), (0, 23), (0, 39)], steps=66)
 
 
 # ---- seeded random configurations ---------------------------------------------
