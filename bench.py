@@ -3,9 +3,13 @@
 A step is the whole hot path for one batch: append one token per sequence,
 quantize any full window, decode one query per (sequence, query head).
 Default workload: Llama-2-7B-shaped layer, batch 32, 32 heads, ragged context
-3072-4096, G=128, R=32, P=32. Several identical, independent layer states are
-stepped round-robin so that consecutive steps touch different memory (the
-256 MB Infinity Cache cannot hold the working set between visits).
+3072-4096, G=128, R=32, P=32. Several independent layer states are stepped
+round-robin so that consecutive steps touch different memory (the 256 MB
+Infinity Cache cannot hold the working set between visits). Their prompt
+lengths are moved by less than G/2 so that the states take turns at the
+quantize step: any window of timed steps then holds the steady-state share of
+quantize launches (one every G/B steps at ragged lengths), and the line reports
+how many the timed steps held.
 
 Prints one JSON line (rank 0, N=1 only).
 """
@@ -14,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -49,12 +54,77 @@ def algorithmic_decode_bytes(layer) -> int:
 
 
 def auto_states(w, lengths) -> int:
-    """States per lap so that one lap reads >= 3 x 256 MB (3..8)."""
+    """States per lap so that one lap reads >= 3 x 256 MB (3..8), raised to the
+    next count coprime with the quantize period (see staggered_lengths)."""
     page = w.group_size * w.head_dim // 2 + 4 * w.head_dim + 4 * w.group_size
     per_head = [(int(L) // w.group_size) * page + (w.pool_size + w.residual + w.group_size // 2) * 4 * w.head_dim
                 for L in lengths]
     state = w.num_kv_heads * sum(per_head)
-    return int(min(8, max(3, -(-3 * 256e6 // max(state, 1)))))
+    n = int(min(8, max(3, -(-3 * 256e6 // max(state, 1)))))
+    period = quantize_period(w)
+    while period and math.gcd(n, period) != 1:
+        n += 1
+    return n
+
+
+def quantize_period(w) -> int:
+    """Steps between two quantize steps of one state in the full-step timing: G / B
+    when ragged lengths spread the B windows evenly over the G phases (0 when B
+    does not divide G), G when every sequence has the same length (the windows
+    fill together)."""
+    G, B = w.group_size, w.batch
+    if w.prefill[0] == w.prefill[1]:
+        return G
+    return G // B if G % B == 0 else 0
+
+
+def staggered_lengths(w, lengths, n_states: int):
+    """Per-state prompt lengths for the full-step timing. A window quantizes
+    every G appended tokens, at a step fixed by its length mod G. Each length
+    is moved by less than G/2 (kept inside a ragged workload's range by whole
+    groups) so that the states, stepped round-robin, take turns at quantizing:
+    - ragged lengths: within a state the B sequences reach a full window at
+      evenly spread steps, one every Pi = G/B steps;
+    - equal lengths: a state's B windows stay in step (they fill together, as
+      in the workload), Pi = G;
+    with S states coprime to Pi, state s's quantize steps fall on the global
+    steps i = S t + s that are multiples of Pi. Every Pi-th global step then
+    quantizes (one sequence, or a whole batch of equal lengths), whatever the
+    first timed step, so a window of K steps holds K/Pi (+-1) quantize steps:
+    the steady-state share. Returns [n_states][B] int64."""
+    G, R, C, B = w.group_size, w.residual, w.residual + w.group_size, w.batch
+    lo, hi = w.prefill
+    L0 = np.asarray(lengths, np.int64)
+    period = quantize_period(w)
+
+    def first_due(L):  # state-step at which a prompt of L tokens first quantizes
+        r = L - G * ((L - R) // G) if L >= R + G else L
+        return (C - 1 - r) % G
+
+    spread = lo != hi
+    order = np.argsort([first_due(int(L)) for L in L0], kind="stable")
+    out = []
+    for s in range(n_states):
+        a_s = (s * G) // (B * n_states) if spread else (s * G) // n_states
+        if period:
+            a_s = next(a for a in range(period) if (n_states * a + s) % period == 0)
+        Ls = L0.copy()
+        for k, b in enumerate(order):
+            # this sequence's quantize step mod G
+            tau = (a_s + (k * G) // B) % G if spread else a_s
+            r = R + (G - 1 - tau) % G            # window after the prompt, in [R, C)
+            L = int(L0[b])
+            d = (r - L) % G
+            if d >= G // 2:
+                d -= G
+            L += d
+            while L > hi and L - G >= max(lo, R + G):
+                L -= G
+            while L < lo and L + G <= hi:
+                L += G
+            Ls[b] = L
+        out.append(Ls)
+    return out
 
 
 def decode_kernel_name(w) -> str:
@@ -102,24 +172,43 @@ def cpu_baseline(w, lengths, budget_s: float = 12.0):
     units taken in order until the time budget is spent; each runs prefill
     (untimed) then decode steps (append + quantize + decode of every query head
     of the unit). Scaled to the full batch: tokens/s = B / (per-unit step time
-    * B * Hkv)."""
+    * B * Hkv). The oracle's quantize step is also timed on its own: every
+    quantize_group call of the first unit's prefill (a full group against a
+    pool)."""
     try:
+        import threadpoolctl
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        threadpoolctl = threadpool_limits = None
     import synth
     from oracle import ott_oracle as O
     nq = w.num_q_heads // w.num_kv_heads
     steps = 8
     t_step, n_unit = 0.0, 0
+    q_times = []
     ctx = threadpool_limits(1) if threadpool_limits else None
+    blas = []
+    if threadpoolctl is not None:
+        blas = [f"{i.get('internal_api')} {i.get('version')} x{i.get('num_threads')}"
+                for i in threadpoolctl.threadpool_info()]
     t_all = time.perf_counter()
     try:
         for b in range(w.batch):
             for h in range(w.num_kv_heads):
                 K, V = synth.kv_stream(w, b, h, int(lengths[b]) + steps)
                 st = O.HeadOracle(w.head_dim, w.group_size, w.residual, w.pool_size)
-                O.run_prefill(st, K[:lengths[b]], V[:lengths[b]])
+                if n_unit == 0:  # time each quantize step of this prefill
+                    qg = st.quantize_group
+
+                    def timed_qg(qg=qg):
+                        t = time.perf_counter()
+                        qg()
+                        q_times.append(time.perf_counter() - t)
+                    st.quantize_group = timed_qg
+                    O.run_prefill(st, K[:lengths[b]], V[:lengths[b]])
+                    del st.quantize_group
+                else:
+                    O.run_prefill(st, K[:lengths[b]], V[:lengths[b]])
                 qs = [synth.query(w, t, b)[h * nq:(h + 1) * nq] for t in range(steps)]
                 sm = 1.0 / np.sqrt(w.head_dim)
                 t0 = time.perf_counter()
@@ -138,11 +227,17 @@ def cpu_baseline(w, lengths, budget_s: float = 12.0):
             ctx.__exit__(None, None, None)
     per_unit = t_step / n_unit
     full_step = per_unit * w.batch * w.num_kv_heads
+    q_mean = float(np.mean(q_times)) if q_times else None
     return {"value": w.batch / full_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_unit} (sequence, KV head) units of {w.name} x {steps} decode steps "
                       f"(append+quantize+decode of {nq} query head(s)), fp64 numpy, 1 thread; "
                       f"scaled to {w.batch}x{w.num_kv_heads} units",
-            "s_per_step": full_step}
+            "s_per_step": full_step,
+            "host_cores": len(os.sched_getaffinity(0)), "blas_threads_used": 1,
+            "blas": blas, "numpy": np.__version__,
+            "quantize_group_s_per_head": q_mean, "quantize_group_calls_timed": len(q_times),
+            "quantize_group_s_per_step": (q_mean * w.batch * w.num_kv_heads / w.group_size
+                                          if q_mean else None)}
 
 
 def time_launches(launch, n_targets: int, stream, min_launches: int = 20) -> float:
@@ -402,8 +497,11 @@ def main():
     lengths = synth.prefill_lengths(w)
     if args.states <= 0:
         args.states = auto_states(w, lengths)
+    # per-state prompt lengths whose windows take turns at quantizing, so that
+    # the timed steps hold the steady-state share of quantize steps
+    state_lengths = staggered_lengths(w, lengths, args.states)
     n_steps_state = (args.warmup + args.steps + args.states - 1) // args.states + 1
-    n_pos = int(lengths.max()) + n_steps_state
+    n_pos = int(max(Ls.max() for Ls in state_lengths)) + n_steps_state
     print(f"[bench] generating {w.name} inputs ({n_pos} positions)", file=sys.stderr, flush=True)
     K, V = synth.kv_all(w, n_pos)
     dev = torch.device("cuda:0")
@@ -412,14 +510,17 @@ def main():
     layers = []
     for i in range(args.states):
         lay = OTTLayer.for_workload(w, max_seq_len=n_pos)
-        lay.prefill(Kd, Vd, lengths)
+        lay.prefill(Kd, Vd, state_lengths[i])
         lay.set_num_splits(args.splits)
         layers.append(lay)
         print(f"[bench] state {i} prefilled", file=sys.stderr, flush=True)
-    # per-state new tokens and queries, resident on the device
+    # per-state new tokens (each state's next positions) and queries, resident on
+    # the device: kt[s][t] = the rows at positions state_lengths[s] + t
     bidx = np.arange(w.batch)
-    kt = np.stack([K[bidx, :, lengths + t][:, :, None, :] for t in range(n_steps_state)])
-    vt = np.stack([V[bidx, :, lengths + t][:, :, None, :] for t in range(n_steps_state)])
+    kt = np.stack([np.stack([K[bidx, :, Ls + t][:, :, None, :] for t in range(n_steps_state)])
+                   for Ls in state_lengths])
+    vt = np.stack([np.stack([V[bidx, :, Ls + t][:, :, None, :] for t in range(n_steps_state)])
+                   for Ls in state_lengths])
     ktd = torch.from_numpy(np.ascontiguousarray(kt)).to(dev)
     vtd = torch.from_numpy(np.ascontiguousarray(vt)).to(dev)
     qd = torch.from_numpy(np.stack([synth.queries(w, t) for t in range(args.warmup + args.steps)])).to(dev)
@@ -439,11 +540,16 @@ def main():
     sp = int(stream.cuda_stream)
     ones = [1] * w.batch
 
+    quantized = [0, 0]  # quantize launches, sequences quantized
+
     def step(i):
-        lay = layers[i % args.states]
+        s = i % args.states
+        lay = layers[s]
         t = i // args.states
-        L.ott_append(lay.handle, ktd[t].data_ptr(), vtd[t].data_ptr(), ones, 1, sp)
-        L.ott_quantize_group(lay.handle, sp)
+        L.ott_append(lay.handle, ktd[s, t].data_ptr(), vtd[s, t].data_ptr(), ones, 1, sp)
+        n = L.ott_quantize_group(lay.handle, sp)
+        quantized[0] += n > 0
+        quantized[1] += n
         return lay
 
     for i in range(args.warmup):
@@ -454,6 +560,7 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    quantized[:] = [0, 0]
     t_start.record(stream)
     for j in range(args.steps):
         i = args.warmup + j
@@ -461,6 +568,9 @@ def main():
         L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
     t_end.record(stream)
     torch.cuda.synchronize()
+    timed_quantize = {"launches": quantized[0], "sequences": quantized[1],
+                      "steady_state_launches_per_step":
+                          round(1.0 / quantize_period(w), 5) if quantize_period(w) else None}
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     tokens_per_s = w.batch * args.steps / (total_ms / 1e3)
@@ -498,14 +608,19 @@ def main():
         cpu = cpu_baseline(w, lengths)
     res = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8e4m3-digit x fp4-code MFMA, fp32 accumulate",
            "data": "synthetic",
            "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                       "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                       "context": f"{w.prefill[0]}-{w.prefill[1]}", "G": w.group_size,
                       "R": w.residual, "P": w.pool_size, "states": args.states,
                       "splits": args.splits or "auto",
-                      "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window"},
+                      "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window",
+                      "step": "append 1 token per sequence + quantize full windows + decode",
+                      "state_lengths": "each state's prompt lengths moved by < G/2 so the states "
+                                       "take turns at quantizing (steady-state share per step)"},
+           "timed_quantize": timed_quantize,
            "roofline": roofline, "cpu_baseline": cpu, "fp16_baseline": fp16}
     print(json.dumps(res), flush=True)
 
