@@ -18,12 +18,15 @@ OTT_OK = 0
 STATUS_NAMES = {
     0: "OTT_OK", 1: "OTT_ERR_INVALID_ARG", 2: "OTT_ERR_UNSUPPORTED",
     3: "OTT_ERR_ARENA_TOO_SMALL", 4: "OTT_ERR_CAPACITY", 5: "OTT_ERR_STATE", 6: "OTT_ERR_HIP",
+    7: "OTT_ERR_SCRATCH_TOO_SMALL",
 }
+FP16_DECODE_SCRATCH_BYTES = 8 << 20  # OTT_FP16_DECODE_SCRATCH_BYTES in include/ott.h
 
 # Every symbol include/ott.h declares.
 EXPORTS = ("ott_init", "ott_append", "ott_quantize_group", "ott_decode", "ott_destroy",
            "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits", "ott_status_string",
-           "ott_fp16_decode", "ott_fp16_decode_workspace", "ott_prefill")
+           "ott_fp16_decode", "ott_fp16_decode_workspace", "ott_prefill",
+           "ott_fp16_decode_noalloc")
 
 
 class ott_config_t(ctypes.Structure):
@@ -77,6 +80,9 @@ def _load() -> ctypes.CDLL:
     lib.ott_fp16_decode.argtypes = [I32, I32, I32, I32, VP, VP, I32, P(I32), VP, VP, ctypes.c_float,
                                     VP, ctypes.c_size_t, I32, VP]
     lib.ott_fp16_decode.restype = ctypes.c_int
+    lib.ott_fp16_decode_noalloc.argtypes = [I32, I32, I32, I32, VP, VP, I32, P(I32), VP, VP,
+                                            ctypes.c_float, I32, VP]
+    lib.ott_fp16_decode_noalloc.restype = ctypes.c_int
     lib.ott_fp16_decode_workspace.argtypes = [I32, I32, I32]
     lib.ott_fp16_decode_workspace.restype = ctypes.c_size_t
     lib.ott_status_string.argtypes = [ctypes.c_int]
@@ -187,6 +193,19 @@ def ott_fp16_decode(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: i
                                ctypes.c_void_p(d_v), max_len, arr, ctypes.c_void_p(d_q),
                                ctypes.c_void_p(d_out), sm_scale, ctypes.c_void_p(d_work),
                                work_bytes, num_splits, ctypes.c_void_p(stream)), "ott_fp16_decode")
+
+
+def ott_fp16_decode_noalloc(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            d_k: int, d_v: int, max_len: int, lens, d_q: int, d_out: int,
+                            sm_scale: float, num_splits: int, stream: int) -> None:
+    if len(lens) != batch:
+        raise ValueError(f"lens has {len(lens)} entries; batch is {batch}")
+    arr = (ctypes.c_int32 * len(lens))(*[int(x) for x in lens])
+    _check(lib.ott_fp16_decode_noalloc(batch, num_q_heads, num_kv_heads, head_dim,
+                                       ctypes.c_void_p(d_k), ctypes.c_void_p(d_v), max_len, arr,
+                                       ctypes.c_void_p(d_q), ctypes.c_void_p(d_out), sm_scale,
+                                       num_splits, ctypes.c_void_p(stream)),
+           "ott_fp16_decode_noalloc")
 
 
 def ott_fp16_decode_workspace(batch: int, num_q_heads: int, num_splits: int) -> int:

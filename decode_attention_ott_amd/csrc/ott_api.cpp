@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -386,17 +387,41 @@ int64_t fp16_decode_slots(int hg) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
-  if (batch <= 0 || num_q_heads <= 0 || num_splits <= 1) return 0;
-  return size_t(batch) * num_q_heads * num_splits * (2 + ott::kHeadDim) * sizeof(float);
+// Split workspace of ott_fp16_decode_noalloc, owned by the library: each GPU
+// the library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[OTT_FP16_DECODE_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchDevices];  // per device; looked up once, with that device current
+
+// Device address of the current device's copy of `scratch` (NULL if the
+// runtime cannot tell).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_addr[dev] = p;
+  }
+  return g_scratch_addr[dev];
 }
 
-ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t head_dim, const void* d_k, const void* d_v, int32_t max_len,
-                             const int32_t* h_len, const void* d_q, void* d_out, float sm_scale,
-                             void* d_work, size_t work_bytes, int32_t num_splits, void* stream) {
+// ott_fp16_decode with its split partials in d_work (work_bytes of it), or,
+// when scratch_addr is given, in the library's scratch (work_bytes = its size;
+// too many splits is OTT_ERR_SCRATCH_TOO_SMALL instead of
+// OTT_ERR_ARENA_TOO_SMALL). Arguments are validated before any HIP call.
+ott_status_t fp16_decode_on(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, const void* d_k, const void* d_v, int32_t max_len,
+                            const int32_t* h_len, const void* d_q, void* d_out, float sm_scale,
+                            void* d_work, size_t work_bytes, int32_t num_splits, void* stream,
+                            void* (*scratch_addr)()) {
   if (batch < 1 || batch > ott::kMaxBatch || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
       num_q_heads % num_kv_heads != 0 || max_len < 1 || num_splits < 0 || !h_len)
     return OTT_ERR_INVALID_ARG;
@@ -413,10 +438,9 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
   }
   // splits: as given, or enough work-groups for one round of the GPU with at
   // least 256 tokens each; never more than the workspace holds
-  const int64_t fit = (d_work == nullptr)
-                          ? 1
-                          : int64_t(work_bytes / (size_t(batch) * num_q_heads * (2 + ott::kHeadDim) *
-                                                  sizeof(float)));
+  const bool library_scratch = scratch_addr != nullptr;
+  const size_t per_split = size_t(batch) * num_q_heads * (2 + ott::kHeadDim) * sizeof(float);
+  const int64_t fit = (d_work == nullptr && !library_scratch) ? 1 : int64_t(work_bytes / per_split);
   int S = num_splits;
   if (S == 0) {
     const int64_t slots = fp16_decode_slots(ott::fp16_heads_per_pass(num_q_heads / num_kv_heads));
@@ -424,14 +448,19 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, (lmax + 255) / 256)));
     S = int(std::min<int64_t>(S, std::max<int64_t>(1, fit)));
   } else if (S > 1 && S > fit) {
-    return OTT_ERR_ARENA_TOO_SMALL;
+    return library_scratch ? OTT_ERR_SCRATCH_TOO_SMALL : OTT_ERR_ARENA_TOO_SMALL;
+  }
+  void* part = d_work;
+  if (library_scratch && S > 1) {
+    part = scratch_addr();
+    if (part == nullptr) return OTT_ERR_HIP;
   }
   ott::Fp16Cache c;
   c.k = static_cast<const __half*>(d_k);
   c.v = static_cast<const __half*>(d_v);
   c.q = static_cast<const __half*>(d_q);
   c.out = static_cast<__half*>(d_out);
-  c.part = static_cast<float*>(d_work);
+  c.part = static_cast<float*>(part);
   c.B = batch;
   c.Hq = num_q_heads;
   c.Hkv = num_kv_heads;
@@ -440,6 +469,33 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
   return ott::launch_fp16_decode(c, lens, S, static_cast<hipStream_t>(stream)) == hipSuccess
              ? OTT_OK
              : OTT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_splits <= 1) return 0;
+  return size_t(batch) * num_q_heads * num_splits * (2 + ott::kHeadDim) * sizeof(float);
+}
+
+ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, const void* d_k, const void* d_v, int32_t max_len,
+                             const int32_t* h_len, const void* d_q, void* d_out, float sm_scale,
+                             void* d_work, size_t work_bytes, int32_t num_splits, void* stream) {
+  return fp16_decode_on(batch, num_q_heads, num_kv_heads, head_dim, d_k, d_v, max_len, h_len, d_q,
+                        d_out, sm_scale, d_work, work_bytes, num_splits, stream, nullptr);
+}
+
+ott_status_t ott_fp16_decode_noalloc(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, const void* d_k, const void* d_v,
+                                     int32_t max_len, const int32_t* h_len, const void* d_q,
+                                     void* d_out, float sm_scale, int32_t num_splits,
+                                     void* stream) {
+  return fp16_decode_on(batch, num_q_heads, num_kv_heads, head_dim, d_k, d_v, max_len, h_len, d_q,
+                        d_out, sm_scale, nullptr, OTT_FP16_DECODE_SCRATCH_BYTES, num_splits,
+                        stream, scratch_on_current_device);
 }
 
 const char* ott_status_string(ott_status_t s) {
@@ -451,6 +507,8 @@ const char* ott_status_string(ott_status_t s) {
     case OTT_ERR_CAPACITY: return "window or sequence capacity exceeded";
     case OTT_ERR_STATE: return "invalid state for this call";
     case OTT_ERR_HIP: return "HIP error (handle poisoned)";
+    case OTT_ERR_SCRATCH_TOO_SMALL:
+      return "request exceeds the library's fixed scratch (OTT_FP16_DECODE_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

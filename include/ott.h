@@ -48,7 +48,8 @@ typedef enum {
   OTT_ERR_ARENA_TOO_SMALL = 3, /* arena_bytes below the required size, or misaligned arena */
   OTT_ERR_CAPACITY = 4,        /* append would overflow the window or max_seq_len */
   OTT_ERR_STATE = 5,           /* decode of a sequence that holds no token */
-  OTT_ERR_HIP = 6              /* a HIP launch failed; the handle is poisoned */
+  OTT_ERR_HIP = 6,             /* a HIP launch failed; the handle is poisoned */
+  OTT_ERR_SCRATCH_TOO_SMALL = 7 /* the request needs more than the library's fixed scratch */
 } ott_status_t;
 
 /* Layer shape and OTT hyper-parameters ([Blog] 3.1-3.3, section 4 and 6). */
@@ -245,6 +246,30 @@ ott_status_t ott_fp16_decode(int32_t batch, int32_t num_q_heads, int32_t num_kv_
                              void* d_work, size_t work_bytes, int32_t num_splits, void* stream);
 /* ott_fp16_decode_workspace - bytes of d_work that num_splits splits need (0 for <= 1). */
 size_t ott_fp16_decode_workspace(int32_t batch, int32_t num_q_heads, int32_t num_splits);
+
+/*
+ * ott_fp16_decode_noalloc - ott_fp16_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results without d_work and
+ * work_bytes. The split partials go to a scratch array the library owns, one
+ * copy per GPU (OTT_FP16_DECODE_SCRATCH_BYTES, held until the process ends);
+ * the call allocates nothing and calls no allocating routine. The caller
+ * still passes inputs and outputs.
+ *   num_splits: 0 = automatic (never more than the scratch holds), 1 = no
+ *   scratch used, n > 1 needs ott_fp16_decode_workspace(batch, Hq, n) <=
+ *   OTT_FP16_DECODE_SCRATCH_BYTES, else OTT_ERR_SCRATCH_TOO_SMALL (nothing
+ *   enqueued).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it needs clearing: each split writes its slot before the
+ * merge reads it). Calls that overlap on one GPU (other streams, other threads)
+ * race on it; the caller must order them.
+ */
+#define OTT_FP16_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+ott_status_t ott_fp16_decode_noalloc(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, const void* d_k, const void* d_v,
+                                     int32_t max_len, const int32_t* h_len, const void* d_q,
+                                     void* d_out, float sm_scale, int32_t num_splits,
+                                     void* stream);
 
 /* ott_status_string - static text for a status code. */
 const char* ott_status_string(ott_status_t s);
