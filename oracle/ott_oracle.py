@@ -386,15 +386,13 @@ def pack_page(page: Page, G: int, d: int) -> bytes:
     kc[:n] = page.k_code
     vc = np.zeros((d, G), np.uint8)
     vc[:, :n] = page.v_code.T
+    def four_per_byte(codes):  # byte j of a row = codes 4j..4j+3, code i at bits 2i
+        return (codes[:, 0::4] | codes[:, 1::4] << 2 | codes[:, 2::4] << 4
+                | codes[:, 3::4] << 6).astype(np.uint8)
+
     out = bytearray()
-    for t in range(G):
-        for j in range(d // 4):
-            out.append(int(kc[t, 4 * j]) | int(kc[t, 4 * j + 1]) << 2
-                       | int(kc[t, 4 * j + 2]) << 4 | int(kc[t, 4 * j + 3]) << 6)
-    for c in range(d):
-        for j in range(G // 4):
-            out.append(int(vc[c, 4 * j]) | int(vc[c, 4 * j + 1]) << 2
-                       | int(vc[c, 4 * j + 2]) << 4 | int(vc[c, 4 * j + 3]) << 6)
+    out += four_per_byte(kc).tobytes()      # token t: bytes of channels 0..d-1
+    out += four_per_byte(vc).tobytes()      # channel c: bytes of slots 0..G-1
     km = np.zeros((d, 2), F16)
     km[:, 0] = page.k_min
     km[:, 1] = page.k_scale
