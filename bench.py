@@ -338,9 +338,13 @@ def sweep_batch(args, batches):
 def accuracy(args, batch: int = 8):
     """Attention-output error of the OTT decode against exact attention over the
     same fp16 tokens (the fp16 baseline kernel), for the plain 2-bit cache
-    (P = 0), the pages' pool size (P = 32) and a larger pool (P = 128), on the
+    (P = 0), the pages' pool size (P = 32) and a larger pool (P = 128), for the
+    comparison pool rules, and for G = 256 with larger R and P, on the
     workload's Key law and on its one-signed outlier-channel variant. The
-    workload's shape with `batch` sequences; one JSON line per setting."""
+    workload's shape with `batch` sequences; one JSON line per setting. The
+    L1 loss is the mean absolute error over every output element (the measure
+    of the pages' retention-criterion comparison); relative L1 divides the summed
+    absolute error by the summed absolute exact output."""
     import torch
     import synth
     from decode_attention_ott_amd import OTTLayer, _lib as L
@@ -377,9 +381,13 @@ def accuracy(args, batch: int = 8):
                               qd.data_ptr(), ref.data_ptr(), 0.0, work.data_ptr(), nbytes, 0, sp)
             refs[name] = (qd, ref)
         # the method's rule at P = 0, 32, 128; the comparison rules of the pages'
-        # Figure 1(c) (largest Key norm, random) at P = 32
-        for P, rule in ((0, 0), (32, 0), (128, 0), (32, 1), (32, 2)):
-            w = base.with_(pool_size=P, retention=rule)
+        # Figure 1(c) (largest Key norm, random) at P = 32; G = 256 with R = 64,
+        # 128 and P = 32, 128 (a larger group needs a larger window and pool)
+        settings = [(128, base.residual, P, rule)
+                    for P, rule in ((0, 0), (32, 0), (128, 0), (32, 1), (32, 2))]
+        settings += [(256, R, P, 0) for R in (64, 128) for P in (32, 128)]
+        for G, R, P, rule in settings:
+            w = base.with_(group_size=G, residual=R, pool_size=P, retention=rule)
             lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()))
             lay.prefill(Kd, Vd, lengths)
             for name, (qd, ref) in refs.items():
@@ -389,11 +397,14 @@ def accuracy(args, batch: int = 8):
                 r = ref.double()
                 e = out.double() - r
                 rel = (e.norm(dim=-1) / r.norm(dim=-1)).flatten()
+                l1 = float(e.abs().mean())
                 print(json.dumps({
                     "accuracy": "attention output vs exact fp16-cache attention",
                     "workload": w.name, "batch": batch, "one_signed_outlier_channels": one_signed,
                     "queries": name, "G": w.group_size, "R": w.residual, "P": P,
                     "retention": ["smallest Key norm", "largest Key norm", "random"][rule],
+                    "l1_loss": round(l1, 7),
+                    "rel_l1": round(float(e.abs().sum() / r.abs().sum()), 5),
                     "rel_l2_total": round(float(e.norm() / r.norm()), 5),
                     "rel_l2_per_head_mean": round(float(rel.mean()), 5),
                     "rel_l2_per_head_max": round(float(rel.max()), 5),
@@ -405,9 +416,11 @@ def accuracy(args, batch: int = 8):
 
 def sweep_params(args):
     """OTT decode-only time for G, R and P varied one at a time around the
-    workload's values (G in {64, 128, 256}, R in {32, 64, 128}, P in {0, 32, 128}):
-    one JSON line per setting with the algorithmic bytes per quantized and per
-    cached token-head, decode time, tokens/s and the HBM fraction."""
+    workload's values (G in {64, 128, 256}, R in {32, 64, 128}, P in {0, 32, 128}),
+    then G = 256 with R in {64, 128} and P in {32, 128} together (a larger group
+    wants a larger window and pool): one JSON line per setting with the
+    algorithmic bytes per quantized and per cached token-head, decode time,
+    tokens/s and the HBM fraction."""
     import torch
     import synth
     from decode_attention_ott_amd import OTTLayer, _lib as L
@@ -424,6 +437,7 @@ def sweep_params(args):
     settings = [dict(group_size=g) for g in (64, 128, 256)]
     settings += [dict(residual=r) for r in (64, 128)]
     settings += [dict(pool_size=p) for p in (0, 128)]
+    settings += [dict(group_size=256, residual=r, pool_size=p) for r in (64, 128) for p in (32, 128)]
     for kw in settings:
         w = base.with_(**kw)
         n_states = auto_states(w, lengths)

@@ -8,13 +8,13 @@ from . import _lib
 from ._lib import (OttError, ott_append, ott_decode, ott_destroy, ott_fp16_decode,
                    ott_fp16_decode_workspace, ott_get_layout,
                    ott_get_seq_state, ott_init, ott_prefill, ott_quantize_group,
-                   ott_set_num_splits,
+                   ott_set_num_splits, ott_step,
                    ott_status_string)
 
 __all__ = ["OTTLayer", "OttError", "ott_init", "ott_append", "ott_quantize_group", "ott_decode",
            "ott_destroy", "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits",
            "ott_status_string", "ott_fp16_decode", "ott_fp16_decode_workspace",
-           "ott_prefill"]
+           "ott_prefill", "ott_step"]
 
 
 def __getattr__(name):

@@ -26,7 +26,7 @@ FP16_DECODE_SCRATCH_BYTES = 8 << 20  # OTT_FP16_DECODE_SCRATCH_BYTES in include/
 EXPORTS = ("ott_init", "ott_append", "ott_quantize_group", "ott_decode", "ott_destroy",
            "ott_get_layout", "ott_get_seq_state", "ott_set_num_splits", "ott_status_string",
            "ott_fp16_decode", "ott_fp16_decode_workspace", "ott_prefill",
-           "ott_fp16_decode_noalloc")
+           "ott_fp16_decode_noalloc", "ott_step")
 
 
 class ott_config_t(ctypes.Structure):
@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.ott_quantize_group.restype = ctypes.c_int
     lib.ott_decode.argtypes = [H, VP, VP, VP]
     lib.ott_decode.restype = ctypes.c_int
+    lib.ott_step.argtypes = [H, VP, VP, VP, VP, VP, P(I32)]
+    lib.ott_step.restype = ctypes.c_int
     lib.ott_destroy.argtypes = [H]
     lib.ott_destroy.restype = None
     lib.ott_get_layout.argtypes = [H, P(ott_layout_t)]
@@ -156,6 +158,15 @@ def ott_prefill(h, d_k: int, d_v: int, lens, max_len: int, stream: int) -> None:
 def ott_decode(h, d_q: int, d_out: int, stream: int) -> None:
     _check(lib.ott_decode(h, ctypes.c_void_p(d_q), ctypes.c_void_p(d_out),
                           ctypes.c_void_p(stream)), "ott_decode")
+
+
+def ott_step(h, d_k: int, d_v: int, d_q: int, d_out: int, stream: int) -> int:
+    """Returns the number of sequences quantized in the step."""
+    n = ctypes.c_int32(0)
+    _check(lib.ott_step(h, ctypes.c_void_p(d_k), ctypes.c_void_p(d_v), ctypes.c_void_p(d_q),
+                        ctypes.c_void_p(d_out), ctypes.c_void_p(stream), ctypes.byref(n)),
+           "ott_step")
+    return int(n.value)
 
 
 def ott_destroy(h) -> None:

@@ -23,6 +23,7 @@ struct ott_ctx {
   ott::HeadOrder order{};  // rebuilt at every one-split decode
   ott::QuantizeList due{};  // rebuilt at every quantize call
   std::vector<int32_t> seq_by_size;
+  std::vector<int32_t> ones;  // n_new of a step that falls back to the separate calls
   bool counters_written = false;  // has a launch on this handle set every head's counters?
   bool poisoned = false;
 };
@@ -108,6 +109,57 @@ ott_status_t after_launch(ott_handle_t h, hipError_t e) {
     return OTT_ERR_HIP;
   }
   return OTT_OK;
+}
+
+// Split count and head order of a decode over the host copy of the counters
+// (plus the step's new token when step.k is set), then the launch.
+ott_status_t launch_decode_planned(ott_handle_t h, const void* d_q, void* d_out,
+                                   const ott::StepArgs& step, void* stream) {
+  const int B = h->cfg.batch;
+  const int64_t extra = step.k ? 1 : 0;
+  auto bytes = [&](int b) {
+    const int64_t pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
+    return int64_t(h->nb[b]) * int64_t(h->lay.page_bytes) +
+           (pc + h->rcnt[b] + extra) * 4 * h->cfg.head_dim;
+  };
+  // bytes of the largest head (pages + fp16 tokens) bound the useful split count
+  int64_t bytes_max = 0;
+  for (int b = 0; b < B; ++b) bytes_max = std::max<int64_t>(bytes_max, bytes(b));
+  int S = h->forced_splits;
+  if (S <= 0) {
+    // as many work-groups as the GPU holds at once, each with at least ~3
+    // pages of work
+    const int64_t heads = int64_t(B) * h->cfg.num_kv_heads;
+    S = int(std::max<int64_t>(1, h->slots / heads));
+    S = int(std::min<int64_t>(S, std::max<int64_t>(1, bytes_max / (3 * int64_t(h->lay.page_bytes)))));
+  }
+  S = std::max(1, std::min(S, h->dev.max_splits));
+  // One split per head and heads of unequal size: deal the heads to CUs
+  // largest first, in snake order over the rounds of `cus` work-groups, so
+  // that each CU's total is about the same.
+  ott::HeadOrder& ord = h->order;
+  ord.n = 0;
+  const int Hkv = h->cfg.num_kv_heads;
+  const int64_t heads = int64_t(B) * Hkv;
+  // (only whole rounds: a partial last round would leave holes in the order)
+  if (S == 1 && heads <= ott::kMaxOrdered && heads > h->cus && heads % h->cus == 0) {
+    std::vector<int32_t>& seq = h->seq_by_size;
+    seq.resize(B);
+    for (int b = 0; b < B; ++b) seq[b] = b;
+    std::stable_sort(seq.begin(), seq.end(), [&](int x, int y) { return bytes(x) > bytes(y); });
+    const int64_t C = h->cus;
+    int64_t p = 0;
+    for (int b : seq) {
+      for (int hh = 0; hh < Hkv; ++hh, ++p) {
+        const int64_t r = p / C, i = p % C;
+        const int64_t slot = r * C + ((r & 1) ? C - 1 - i : i);
+        ord.bh[slot] = uint16_t(b * Hkv + hh);
+      }
+    }
+    ord.n = int32_t(heads);
+  }
+  return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, ord, step,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -228,6 +280,7 @@ ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_qua
   const int B = h->cfg.batch, C = h->dev.C, G = h->dev.G;
   ott::QuantizeList& due = h->due;
   due.n = 0;
+  due.deferred = 0;
   for (int b = 0; b < B; ++b)
     if (h->rcnt[b] >= C) due.b[due.n++] = uint16_t(b);
   const int ready = due.n;
@@ -285,54 +338,69 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
   ott_status_t st = check_handle(h);
   if (st != OTT_OK) return st;
   if (!d_q || !d_out || misaligned16(d_q) || misaligned16(d_out)) return OTT_ERR_INVALID_ARG;
-  const int B = h->cfg.batch;
-  // bytes of the largest head (pages + fp16 tokens) bound the useful split count
-  int64_t bytes_max = 0;
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < h->cfg.batch; ++b)
     if (h->L[b] == 0) return OTT_ERR_STATE;
-    const int64_t pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
-    bytes_max = std::max<int64_t>(bytes_max, int64_t(h->nb[b]) * int64_t(h->lay.page_bytes) +
-                                                 (pc + h->rcnt[b]) * 4 * h->cfg.head_dim);
+  ott::StepArgs step{};
+  return launch_decode_planned(h, d_q, d_out, step, stream);
+}
+
+ott_status_t ott_step(ott_handle_t h, const void* d_k, const void* d_v, const void* d_q,
+                      void* d_out, void* stream, int32_t* n_seq_quantized) {
+  ott_status_t st = check_handle(h);
+  if (st != OTT_OK) return st;
+  if (!d_k || !d_v || !d_q || !d_out || misaligned16(d_k) || misaligned16(d_v) ||
+      misaligned16(d_q) || misaligned16(d_out))
+    return OTT_ERR_INVALID_ARG;
+  const int B = h->cfg.batch, C = h->dev.C, G = h->dev.G, R = h->dev.R;
+  for (int b = 0; b < B; ++b) {
+    if (h->rcnt[b] >= C) return OTT_ERR_STATE;  // a full window: ott_quantize_group first
+    if (int64_t(h->L[b]) + 1 > h->cfg.max_seq_len) return OTT_ERR_CAPACITY;
   }
-  int S = h->forced_splits;
-  if (S <= 0) {
-    // as many work-groups as the GPU holds at once, each with at least ~3
-    // pages of work
-    const int64_t heads = int64_t(B) * h->cfg.num_kv_heads;
-    S = int(std::max<int64_t>(1, h->slots / heads));
-    S = int(std::min<int64_t>(S, std::max<int64_t>(1, bytes_max / (3 * int64_t(h->lay.page_bytes)))));
+  if (n_seq_quantized) *n_seq_quantized = 0;
+  if (R == 0 || !h->counters_written) {
+    // With R = 0 the new token belongs to the group a full window quantizes;
+    // before any launch the counters are not set yet: the separate calls.
+    h->ones.assign(size_t(B), 1);
+    st = ott_append(h, d_k, d_v, h->ones.data(), 1, stream);
+    if (st != OTT_OK) return st;
+    st = ott_quantize_group(h, stream, n_seq_quantized);
+    if (st != OTT_OK) return st;
+    return ott_decode(h, d_q, d_out, stream);
   }
-  S = std::max(1, std::min(S, h->dev.max_splits));
-  // One split per head and heads of unequal size: deal the heads to CUs
-  // largest first, in snake order over the rounds of `cus` work-groups, so
-  // that each CU's total is about the same.
-  ott::HeadOrder& ord = h->order;
-  ord.n = 0;
-  const int Hkv = h->cfg.num_kv_heads;
-  const int64_t heads = int64_t(B) * Hkv;
-  // (only whole rounds: a partial last round would leave holes in the order)
-  if (S == 1 && heads <= ott::kMaxOrdered && heads > h->cus && heads % h->cus == 0) {
-    std::vector<int32_t>& seq = h->seq_by_size;
-    seq.resize(B);
-    for (int b = 0; b < B; ++b) seq[b] = b;
-    auto bytes = [&](int b) {
-      const int64_t pc = std::min<int64_t>(h->cfg.pool_size, int64_t(h->cfg.group_size) * h->nb[b]);
-      return int64_t(h->nb[b]) * int64_t(h->lay.page_bytes) + (pc + h->rcnt[b]) * 4 * h->cfg.head_dim;
-    };
-    std::stable_sort(seq.begin(), seq.end(), [&](int x, int y) { return bytes(x) > bytes(y); });
-    const int64_t C = h->cus;
-    int64_t p = 0;
-    for (int b : seq) {
-      for (int hh = 0; hh < Hkv; ++hh, ++p) {
-        const int64_t r = p / C, i = p % C;
-        const int64_t slot = r * C + ((r & 1) ? C - 1 - i : i);
-        ord.bh[slot] = uint16_t(b * Hkv + hh);
-      }
+  // A window holding C - 1 tokens is full after this step's append; its group
+  // (the G oldest tokens) does not include the new one when R >= 1, so it is
+  // quantized first and the decode makes the page visible and appends.
+  ott::QuantizeList& due = h->due;
+  due.n = 0;
+  due.deferred = 1;
+  ott::StepArgs step{};
+  step.k = static_cast<const __half*>(d_k);
+  step.v = static_cast<const __half*>(d_v);
+  for (int b = 0; b < B; ++b) {
+    if (h->rcnt[b] + 1 >= C) {
+      due.b[due.n++] = uint16_t(b);
+      step.adv[b >> 5] |= 1u << (b & 31);
     }
-    ord.n = int32_t(heads);
   }
-  return after_launch(h, ott::launch_decode(h->dev, d_q, d_out, S, ord,
-                                            static_cast<hipStream_t>(stream)));
+  if (due.n > 0) {
+    st = after_launch(h, ott::launch_quantize(h->dev, due, static_cast<hipStream_t>(stream)));
+    if (st != OTT_OK) return st;
+  }
+  // the host copy of the counters as the decode sees them (after the quantize
+  // step, before the append), then after the append
+  for (int i = 0; i < due.n; ++i) {
+    const int b = due.b[i];
+    h->head[b] = (h->head[b] + G) % C;
+    h->rcnt[b] -= G;
+    h->nb[b] += 1;
+  }
+  st = launch_decode_planned(h, d_q, d_out, step, stream);
+  for (int b = 0; b < B; ++b) {
+    h->L[b] += 1;
+    h->rcnt[b] += 1;
+  }
+  if (st == OTT_OK && n_seq_quantized) *n_seq_quantized = due.n;
+  return st;
 }
 
 void ott_destroy(ott_handle_t h) { delete h; }

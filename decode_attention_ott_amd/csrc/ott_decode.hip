@@ -252,7 +252,7 @@ struct alignas(16) WaveLds {
 template <int G>
 __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, const __half* __restrict__ q,
                                                      __half* __restrict__ out, int S,
-                                                     HeadOrder order) {
+                                                     HeadOrder order, StepArgs step) {
   __shared__ WaveLds<G> lds_all[kWaves];
   __shared__ float mg_m[kWaves], mg_l[kWaves];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -262,14 +262,15 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);  // = b * H + h
   const int b = bh / a.Hkv;
 
-  const int32_t* ctr = counters(a, bh);
-  const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
+  const HeadCtr hc = head_counters(a, step, b, bh);
+  const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
   const int pc = min(a.P, a.G * nb);
-  const Split sp = split_of(nb, pc + r_cnt, a.page_bytes, s, S);
+  const int n_new = step.k ? 1 : 0;  // a fused step's new token, after the window
+  const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
   const int p1 = sp.p1, t1 = sp.t1;
   const int buf = nb & 1;
   const Fp16Src src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
-                    head, a.C};
+                    head, a.C, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
   const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
@@ -358,15 +359,29 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
         part[1] = Ls;
       }
     }
+  } else if (step.k && S == 1 && threadIdx.x < D + 32) {
+    // a fused step with one split: this work-group is the head's only reader
+    // of its counters, so it stores the new token and the counters itself
+    step_store(a, step, bh, hc, threadIdx.x - D);
   }
 }
 
-// Merge of the S split partial states of each (sequence, query head).
-__global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict__ out, int S) {
+// Merge of the S split partial states of each (sequence, query head). In a
+// fused step the work-group of each KV head's first query head also stores the
+// step's new token and the head's counters (every split has read them).
+__global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict__ out, int S,
+                                                    StepArgs step) {
   const int bq = blockIdx.x;  // b * Hq + qh
   const float* part = reinterpret_cast<const float*>(a.base + a.off_partials) +
                       size_t(bq) * a.max_splits * (2 + D);
   out[size_t(bq) * D + threadIdx.x] = __float2half_rn(merge_partials(part, S, threadIdx.x));
+  if (step.k != nullptr && threadIdx.x < 32) {
+    const int NQ = a.Hq / a.Hkv, b = bq / a.Hq, qh = bq % a.Hq;
+    if (qh % NQ == 0) {
+      const int bh = b * a.Hkv + qh / NQ;
+      step_store(a, step, bh, head_counters(a, step, b, bh), threadIdx.x);
+    }
+  }
 }
 
 }  // namespace
@@ -385,24 +400,24 @@ int decode_wgs_per_cu(const Arena& a) {
 }
 
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, const HeadOrder& order,
-                         hipStream_t s) {
+                         const StepArgs& step, hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);
   hipError_t e;
   if (a.Hq != a.Hkv) {
-    e = launch_decode_gqa(a, q, out, S, order, s);
+    e = launch_decode_gqa(a, q, out, S, order, step, s);
   } else {
     const dim3 grid(unsigned(a.B) * a.Hkv * S);
     switch (a.G) {
-      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
-      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
-      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order); break;
+      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
+      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
+      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
   }
   if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(a.B) * a.Hq), dim3(D), 0, s, a, oh, S);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(a.B) * a.Hq), dim3(D), 0, s, a, oh, S, step);
   return hipGetLastError();
 }
 

@@ -156,20 +156,72 @@ __device__ __forceinline__ float quad_sum(float x) {
 // 16 lanes share one token (lane&15 takes channels 8*(lane&15)..+7), so every
 // load instruction reads 4 whole 256-byte rows. Scores reduce inside the row
 // with DPP; the row then holds the token's weight for its V accumulation.
+// In a fused step, token n_old (the last) is the step's new token, read from
+// the step's input rows nk/nv.
 struct Fp16Src {
   const __half* pk;
   const __half* pv;
   const __half* rk;
   const __half* rv;
   int pc, head, C;
+  int n_old;  // pool + window tokens
+  const __half* nk;
+  const __half* nv;
   __device__ __forceinline__ size_t row(int i) const {
     if (i < pc) return size_t(i) * D;
     const int x = head + i - pc;  // < 2C: head < C and i - pc < r_cnt <= C
     return size_t(x >= C ? x - C : x) * D;
   }
-  __device__ __forceinline__ const __half* k(int i) const { return (i < pc ? pk : rk) + row(i); }
-  __device__ __forceinline__ const __half* v(int i) const { return (i < pc ? pv : rv) + row(i); }
+  __device__ __forceinline__ const __half* k(int i) const {
+    return i >= n_old ? nk : (i < pc ? pk : rk) + row(i);
+  }
+  __device__ __forceinline__ const __half* v(int i) const {
+    return i >= n_old ? nv : (i < pc ? pv : rv) + row(i);
+  }
 };
+
+// Counters of (sequence, KV head) bh as a step's decode sees them: a quantize
+// step that becomes visible in this step advances the window and page count.
+struct HeadCtr {
+  int L, r_cnt, head, nb;
+  bool adv;
+};
+__device__ __forceinline__ bool step_adv(const StepArgs& st, int b) {
+  return st.k != nullptr && ((st.adv[b >> 5] >> (b & 31)) & 1u);
+}
+__device__ __forceinline__ HeadCtr head_counters(const Arena& a, const StepArgs& st, int b, int bh) {
+  const int32_t* ctr = counters(a, bh);
+  HeadCtr c{ctr[0], ctr[1], ctr[2], ctr[3], step_adv(st, b)};
+  if (c.adv) {
+    c.r_cnt -= a.G;
+    c.head += a.G;
+    if (c.head >= a.C) c.head -= a.C;
+    c.nb += 1;
+  }
+  return c;
+}
+
+// The step's new token of bh into window slot (head + r_cnt) % C, and the
+// head's counters; called by lanes t = 0..31 of the head's single writer.
+// The window head and page count are written only when they changed, so a
+// quantize step reading them elsewhere never races with this write.
+__device__ __forceinline__ void step_store(const Arena& a, const StepArgs& st, int bh,
+                                           const HeadCtr& c, int t) {
+  int slot = c.head + c.r_cnt;
+  if (slot >= a.C) slot -= a.C;
+  const uint4* src = reinterpret_cast<const uint4*>((t < 16 ? st.k : st.v) + size_t(bh) * D);
+  uint4* dst = reinterpret_cast<uint4*>((t < 16 ? ring_k(a, bh) : ring_v(a, bh)) + size_t(slot) * D);
+  dst[t & 15] = src[t & 15];
+  if (t == 0) {
+    int32_t* ctr = counters(a, bh);
+    ctr[0] = c.L + 1;
+    ctr[1] = c.r_cnt + 1;
+    if (c.adv) {
+      ctr[2] = c.head;
+      ctr[3] = c.nb;
+    }
+  }
+}
 
 constexpr int kF16Pass = 4;                 // 4 tokens per pass
 constexpr int kF16Chunk = 4 * kF16Pass;     // tokens per chunk

@@ -316,7 +316,8 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
 // not written.
 template <int G, int NA>
 __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_gqa_kernel(
-    Arena a, const __half* __restrict__ q, __half* __restrict__ out, int S, HeadOrder order) {
+    Arena a, const __half* __restrict__ q, __half* __restrict__ out, int S, HeadOrder order,
+    StepArgs step) {
   constexpr int QB = 4 * NA;
   __shared__ GxLds<G, NA> lds_all[kWaves];
   __shared__ float mg_m[kWaves][QB], mg_l[kWaves][QB];
@@ -329,13 +330,14 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
 
-  const int32_t* ctr = counters(a, bh);
-  const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
+  const HeadCtr hc = head_counters(a, step, b, bh);
+  const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
   const int pc = min(a.P, a.G * nb);
-  const Split sp = split_of(nb, pc + r_cnt, a.page_bytes, s, S);
+  const int n_new = step.k ? 1 : 0;  // a fused step's new token, after the window
+  const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
   const int buf = nb & 1;
   const Fp16Src src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
-                    head, a.C};
+                    head, a.C, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
   const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
@@ -474,17 +476,20 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
     }
     __syncthreads();
   }
+  // a fused step with one split: this work-group is the head's only reader of
+  // its counters, so it stores the new token and the counters itself
+  if (step.k && S == 1 && threadIdx.x < 32) step_store(a, step, bh, hc, threadIdx.x);
 }
 
 template <int G>
 hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, const HeadOrder& order,
-                    hipStream_t s) {
+                    const StepArgs& step, hipStream_t s) {
   const int NQ = a.Hq / a.Hkv;
   const dim3 grid(unsigned(a.B) * a.Hkv * S), block(64 * kWaves);
   if (NQ % 8 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S, order);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S, order, step);
   } else {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 1>), grid, block, 0, s, a, q, out, S, order);
+    hipLaunchKernelGGL((decode_gqa_kernel<G, 1>), grid, block, 0, s, a, q, out, S, order, step);
   }
   return hipGetLastError();
 }
@@ -512,13 +517,13 @@ int decode_gqa_wgs_per_cu(const Arena& a) {
 }
 
 hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int S,
-                             const HeadOrder& order, hipStream_t s) {
+                             const HeadOrder& order, const StepArgs& step, hipStream_t s) {
   const __half* qh = static_cast<const __half*>(q);
   __half* oh = static_cast<__half*>(out);
   switch (a.G) {
-    case 64: return launch_g<64>(a, qh, oh, S, order, s);
-    case 128: return launch_g<128>(a, qh, oh, S, order, s);
-    case 256: return launch_g<256>(a, qh, oh, S, order, s);
+    case 64: return launch_g<64>(a, qh, oh, S, order, step, s);
+    case 128: return launch_g<128>(a, qh, oh, S, order, step, s);
+    case 256: return launch_g<256>(a, qh, oh, S, order, step, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -50,9 +50,26 @@ struct HeadOrder {
 hipError_t launch_append(const Arena& a, const void* k, const void* v, const AppendCounts& n,
                          hipStream_t s);
 // The sequences whose window is full at an ott_quantize_group call.
+// deferred = 0: the kernel checks the window is full and advances the counters.
+// deferred = 1 (a fused step): the host has chosen the sequences; the kernel
+// reads only the window head and page count, and the step's decode makes the
+// new page visible (it applies the counter advance, see StepArgs).
 struct QuantizeList {
   int32_t n;
+  int32_t deferred;
   uint16_t b[kMaxBatch];
+};
+// The append half of a fused step (ott_step), carried by the decode launch:
+// one new token per sequence, rows k/v [B][Hkv][D] (k == NULL: a plain decode).
+// Sequences with their bit set in adv had a quantize step in this step: the
+// decode first advances their counters (window head + G, window count - G,
+// pages + 1). The new token is the last fp16 token the decode attends (read
+// from k/v); the head's single writer (the one-split work-group, or the split
+// merge) then stores it in window slot (head + r_cnt) % C and writes the counters.
+struct StepArgs {
+  const __half* k;
+  const __half* v;
+  uint32_t adv[kMaxBatch / 32];
 };
 hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s);
 // Prompt lengths of an ott_prefill call.
@@ -64,11 +81,11 @@ struct PrefillLens {
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
                           const PrefillLens& lens, int max_pages, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
-                         const HeadOrder& order, hipStream_t s);
+                         const HeadOrder& order, const StepArgs& step, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it
 // writes the output (one split) or the split partials like launch_decode.
 hipError_t launch_decode_gqa(const Arena& a, const void* q, void* out, int num_splits,
-                             const HeadOrder& order, hipStream_t s);
+                             const HeadOrder& order, const StepArgs& step, hipStream_t s);
 // Work-groups of the decode kernel this arena's shape launches that fit on
 // one CU at once (0 if the runtime cannot tell).
 int decode_wgs_per_cu(const Arena& a);

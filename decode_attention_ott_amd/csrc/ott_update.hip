@@ -488,6 +488,13 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
   const int h = blockIdx.x, b = due.b[blockIdx.y];
   const int bh = b * a.Hkv + h;
   int32_t* ctr = counters(a, bh);
+  if (due.deferred) {
+    // a fused step: the host picked this sequence; the step's decode advances
+    // the counters (it may be writing the window count and length meanwhile,
+    // so only the window head and page count are read here)
+    quantize_step(a, bh, ctr[3], ring_k(a, bh), ring_v(a, bh), ctr[2], a.C, lds_raw);
+    return;
+  }
   const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
   if (r_cnt < a.C) return;  // window not full: nothing to do for this sequence
   quantize_step(a, bh, nb, ring_k(a, bh), ring_v(a, bh), head, a.C, lds_raw);

@@ -75,6 +75,23 @@ class OTTLayer:
         L.ott_decode(self.handle, q.data_ptr(), out.data_ptr(), _stream())
         return out
 
+    def step(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+             out: Optional[torch.Tensor] = None):
+        """One decode step (append one token per sequence, quantize full windows,
+        decode) through ott_step. k, v: fp16 [B, Hkv, 1, d]; q: fp16 [B, Hq, d].
+        Returns (out, sequences quantized)."""
+        self._check_kv(k, v)
+        if k.shape[2] != 1:
+            raise ValueError("a step appends one token per sequence")
+        if q.dtype != torch.float16 or q.device != self.device or not q.is_contiguous() \
+                or tuple(q.shape) != (self.B, self.Hq, self.d):
+            raise ValueError(f"q must be contiguous fp16 [{self.B}, {self.Hq}, {self.d}]")
+        if out is None:
+            out = torch.empty_like(q)
+        n = L.ott_step(self.handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), out.data_ptr(),
+                       _stream())
+        return out, n
+
     def set_num_splits(self, s: int) -> None:
         L.ott_set_num_splits(self.handle, s)
 

@@ -201,6 +201,29 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
  */
 ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream);
 
+/*
+ * ott_step - one whole decode step in as few launches as possible: the same
+ * state and output as ott_append (one token per sequence), ott_quantize_group,
+ * ott_decode ([Blog] flowchart: a quantization stage every G tokens, a decoding
+ * stage every token; [Abs] Figure 2).
+ *   d_k, d_v : device fp16 [B][Hkv][d], the new token of every sequence (position
+ *              L_b); d_q, d_out : device fp16 [B][Hq][d]. All 16-byte aligned, else
+ *              OTT_ERR_INVALID_ARG. The k/v rows are copied into the window.
+ *   *n_seq_quantized (may be NULL) receives the number of sequences whose group
+ *   was quantized in this step.
+ *   How: with R >= 1 a window holding R+G-1 tokens is quantized before the
+ *   append (its G oldest tokens, the group, do not include the new one, so the
+ *   result is the same); the decode then attends the new token from d_k/d_v and
+ *   the head's single writer stores it in the window. One launch when no window
+ *   fills (two with split-K), one more when one does. With R = 0 (the new token
+ *   joins the group) or before any append/prefill, the three calls are made.
+ *   OTT_ERR_STATE if some window already holds R+G tokens (call
+ *   ott_quantize_group first); OTT_ERR_CAPACITY if some L_b + 1 > max_seq_len.
+ *   Nothing is enqueued on error.
+ */
+ott_status_t ott_step(ott_handle_t h, const void* d_k, const void* d_v, const void* d_q,
+                      void* d_out, void* stream, int32_t* n_seq_quantized);
+
 /* ott_destroy - free the host handle (the arena stays the caller's). NULL is a no-op. */
 void ott_destroy(ott_handle_t h);
 

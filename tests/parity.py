@@ -74,13 +74,16 @@ def run_case(w: synth.Workload, steps: Optional[int] = None,
              heads: Optional[Sequence[Tuple[int, int]]] = None,
              lengths: Optional[Sequence[int]] = None, splits: Optional[Sequence[int]] = None,
              q_scale: float = 1.0, state_every_step: bool = False, check_prefill: bool = True,
-             plant=None):
+             plant=None, step_calls: Optional[str] = None):
     """Prefill + `steps` decode steps on the GPU and in the oracle.
 
     heads: the (sequence, KV head) pairs the oracle follows (default: all).
     splits: split-K factors each decode is run with (default: automatic).
     plant: optional plant(K, V) that edits the drawn fp16 [B, Hkv, pos, d] inputs
     in place before either side sees them.
+    step_calls: None = each step as ott_append, ott_quantize_group, ott_decode;
+    "step" = each step as one ott_step (its decode with the first split count,
+    the others as ott_decode afterwards); "mixed" = ott_step on even steps.
     Returns the worst (max abs, rel L2) seen.
     """
     import torch
@@ -91,7 +94,7 @@ def run_case(w: synth.Workload, steps: Optional[int] = None,
     n_pos = int(lengths.max()) + steps
     log(f"[parity] {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} G={w.group_size}"
         f" R={w.residual} P={w.pool_size} L={lengths.min()}..{lengths.max()} steps={steps}"
-        f" splits={splits} q_scale={q_scale}")
+        f" splits={splits} q_scale={q_scale} calls={step_calls or 'separate'}")
     K, V = synth.kv_all(w, n_pos)
     if plant is not None:
         plant(K, V)
@@ -118,20 +121,30 @@ def run_case(w: synth.Workload, steps: Optional[int] = None,
         pos = lengths + t
         kt = np.ascontiguousarray(K[bidx, :, pos][:, :, None, :])
         vt = np.ascontiguousarray(V[bidx, :, pos][:, :, None, :])
-        layer.append(torch.from_numpy(kt).cuda(), torch.from_numpy(vt).cuda())
-        layer.quantize_group()
+        q = (synth.queries(w, t).astype(np.float32) * np.float32(q_scale)).astype(np.float16)
+        qd = torch.from_numpy(q).cuda()
+        fused = step_calls == "step" or (step_calls == "mixed" and t % 2 == 0)
+        split_list = list(splits or [0])
+        if fused:
+            layer.set_num_splits(split_list[0])
+            out_step, _ = layer.step(torch.from_numpy(kt).cuda(), torch.from_numpy(vt).cuda(), qd)
+        else:
+            layer.append(torch.from_numpy(kt).cuda(), torch.from_numpy(vt).cuda())
+            layer.quantize_group()
         for b, h in heads:
             O.step(orc.head(b, h), K[b, h, pos[b]], V[b, h, pos[b]])
         if state_every_step:
             check_state(layer, orc, heads, f"step {t}")
-        q = (synth.queries(w, t).astype(np.float32) * np.float32(q_scale)).astype(np.float16)
-        qd = torch.from_numpy(q).cuda()
         ref = np.stack([orc.decode(b, qh, q[b, qh]) for b, qh in qrows])
-        for s in (splits or [0]):
-            layer.set_num_splits(s)
-            out = layer.decode(qd).cpu().numpy()
+        for i, s in enumerate(split_list):
+            if fused and i == 0:
+                out = out_step.cpu().numpy()
+            else:
+                layer.set_num_splits(s)
+                out = layer.decode(qd).cpu().numpy()
             got = np.stack([out[b, qh] for b, qh in qrows])
-            mx, rel = compare_outputs(got, ref, f"{w.name} step {t} splits {s}")
+            mx, rel = compare_outputs(got, ref, f"{w.name} step {t} splits {s}"
+                                                + (" (ott_step)" if fused and i == 0 else ""))
             worst = (max(worst[0], mx), max(worst[1], rel))
     layer.set_num_splits(0)
     check_state(layer, orc, heads, "end")

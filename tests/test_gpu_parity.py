@@ -41,6 +41,7 @@ def test_tiny_every_step():
     (64, 5, 3, (333, 333), 20),       # odd window and pool sizes
     (128, 128, 32, (760, 760), 12),   # R=128: window 248 of 256, a quantize at step 7
     (256, 128, 32, (1146, 1146), 10), # G=256, R=128: window 378 of 384, a quantize at step 5
+    (256, 128, 128, (1146, 1146), 10),  # G=256, R=128, P=128 (the coupled setting)
     (256, 64, 512, (1082, 1082), 10), # P=512 at G=256: quantize LDS above 64 KiB, a step at 5
 ])
 def test_parameters(G, R, P, L, steps):
