@@ -1,15 +1,17 @@
 """Benchmark of the OTT decode step on one MI355X.
 
 A step is the whole hot path for one batch: append one token per sequence,
-quantize any full window, decode one query per (sequence, query head).
+quantize any full window, decode one query per (sequence, query head), in one
+ott_step call (--separate-calls: the three calls).
 Default workload: Llama-2-7B-shaped layer, batch 32, 32 heads, ragged context
 3072-4096, G=128, R=32, P=32. Several independent layer states are stepped
 round-robin so that consecutive steps touch different memory (the 256 MB
 Infinity Cache cannot hold the working set between visits). Their prompt
 lengths are moved by less than G/2 so that the states take turns at the
 quantize step: any window of timed steps then holds the steady-state share of
-quantize launches (one every G/B steps at ragged lengths), and the line reports
-how many the timed steps held.
+quantize steps (one every G/B steps at ragged lengths), and the line reports
+how many the timed steps held. (ott_step runs the quantize work of every
+window whose group is complete in one launch, so launches are rarer.)
 
 Prints one JSON line (rank 0, N=1 only).
 """
@@ -475,6 +477,9 @@ def main():
                          "over them reads >= 3 x 256 MB, the Infinity Cache size; 3..8)")
     ap.add_argument("--splits", type=int, default=0, help="split-K factor (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time each step as ott_append + ott_quantize_group + ott_decode instead "
+                         "of one ott_step")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before warm-up, one device-to-device copy of this many MiB; its "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE readings calibrate the counters")
@@ -554,21 +559,27 @@ def main():
     sp = int(stream.cuda_stream)
     ones = [1] * w.batch
 
-    quantized = [0, 0]  # quantize launches, sequences quantized
+    quantized = [0, 0]  # steps whose decode sees a new page, sequences quantized
 
     def step(i):
+        """One step of state i % states: ott_step (append + quantize + decode in
+        one call), or the three calls with --separate-calls."""
         s = i % args.states
         lay = layers[s]
         t = i // args.states
-        L.ott_append(lay.handle, ktd[s, t].data_ptr(), vtd[s, t].data_ptr(), ones, 1, sp)
-        n = L.ott_quantize_group(lay.handle, sp)
+        if args.separate_calls:
+            L.ott_append(lay.handle, ktd[s, t].data_ptr(), vtd[s, t].data_ptr(), ones, 1, sp)
+            n = L.ott_quantize_group(lay.handle, sp)
+            L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
+        else:
+            n = L.ott_step(lay.handle, ktd[s, t].data_ptr(), vtd[s, t].data_ptr(), qd[i].data_ptr(),
+                           outd.data_ptr(), sp)
         quantized[0] += n > 0
         quantized[1] += n
         return lay
 
     for i in range(args.warmup):
-        lay = step(i)
-        L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
+        step(i)
     torch.cuda.synchronize()
 
     t_start = torch.cuda.Event(enable_timing=True)
@@ -577,13 +588,13 @@ def main():
     quantized[:] = [0, 0]
     t_start.record(stream)
     for j in range(args.steps):
-        i = args.warmup + j
-        lay = step(i)
-        L.ott_decode(lay.handle, qd[i].data_ptr(), outd.data_ptr(), sp)
+        step(args.warmup + j)
     t_end.record(stream)
     torch.cuda.synchronize()
-    timed_quantize = {"launches": quantized[0], "sequences": quantized[1],
-                      "steady_state_launches_per_step":
+    # quantize steps (a window's group becoming a page) in the timed steps; with
+    # ott_step their work runs in fewer launches (every complete group at once)
+    timed_quantize = {"steps_with_a_quantize": quantized[0], "sequences": quantized[1],
+                      "steady_state_steps_with_a_quantize_per_step":
                           round(1.0 / quantize_period(w), 5) if quantize_period(w) else None}
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
@@ -631,7 +642,9 @@ def main():
                       "R": w.residual, "P": w.pool_size, "states": args.states,
                       "splits": args.splits or "auto",
                       "storage": "2-bit K/V codes, fp16 min/scale, fp16 pool and window",
-                      "step": "append 1 token per sequence + quantize full windows + decode",
+                      "step": "append 1 token per sequence + quantize full windows + decode, as "
+                              + ("ott_append + ott_quantize_group + ott_decode" if args.separate_calls
+                                 else "one ott_step"),
                       "state_lengths": "each state's prompt lengths moved by < G/2 so the states "
                                        "take turns at quantizing (steady-state share per step)"},
            "timed_quantize": timed_quantize,

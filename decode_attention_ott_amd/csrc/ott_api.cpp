@@ -24,6 +24,10 @@ struct ott_ctx {
   ott::QuantizeList due{};  // rebuilt at every quantize call
   std::vector<int32_t> seq_by_size;
   std::vector<int32_t> ones;  // n_new of a step that falls back to the separate calls
+  // pending[b]: ott_step already quantized sequence b's next group (page nb and
+  // the other pool buffer are written, not yet visible); its due step's decode
+  // makes them visible. Cleared by every call that changes state otherwise.
+  std::vector<uint8_t> pending;
   bool counters_written = false;  // has a launch on this handle set every head's counters?
   bool poisoned = false;
 };
@@ -217,6 +221,7 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   h->rcnt.assign(nb, 0);
   h->head.assign(nb, 0);
   h->nb.assign(nb, 0);
+  h->pending.assign(nb, 0);
   {
     // one round of decode work-groups fills the GPU: CUs x work-groups per CU
     int dev = 0, cus = 0;
@@ -228,6 +233,11 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
     if (wpc <= 0) wpc = 4;
     h->slots = int64_t(cus) * wpc;
     h->cus = cus;
+    // the LDS a quantize work-group may opt into (0 if the runtime cannot tell)
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess)
+      lds = 0;
+    a.lds_max = lds;
   }
   // Nothing is written to the arena here: the first ott_append or ott_prefill
   // launch sets every head's counters on the caller's stream.
@@ -256,6 +266,7 @@ ott_status_t ott_append(ott_handle_t h, const void* d_k, const void* d_v, const 
     if (h->rcnt[b] + n > C) return OTT_ERR_CAPACITY;
     if (int64_t(h->L[b]) + n > h->cfg.max_seq_len) return OTT_ERR_CAPACITY;
   }
+  std::fill(h->pending.begin(), h->pending.end(), 0);
   ott::AppendCounts cnt{};
   cnt.max_new = max_new;
   cnt.uniform = uniform ? h_n_new[0] : -1;
@@ -286,6 +297,7 @@ ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_qua
   const int ready = due.n;
   if (n_seq_quantized) *n_seq_quantized = 0;
   if (ready == 0) return OTT_OK;
+  std::fill(h->pending.begin(), h->pending.end(), 0);
   st = after_launch(h, ott::launch_quantize(h->dev, due, static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
   for (int b = 0; b < B; ++b) {
@@ -316,6 +328,7 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
   }
   if (!any) return OTT_OK;
   if (!d_k || !d_v || misaligned16(d_k) || misaligned16(d_v)) return OTT_ERR_INVALID_ARG;
+  std::fill(h->pending.begin(), h->pending.end(), 0);
   int max_pages = 0;
   for (int b = 0; b < B; ++b)
     if (h_len[b] >= R + G) max_pages = std::max(max_pages, (h_len[b] - R) / G);
@@ -367,39 +380,53 @@ ott_status_t ott_step(ott_handle_t h, const void* d_k, const void* d_v, const vo
     if (st != OTT_OK) return st;
     return ott_decode(h, d_q, d_out, stream);
   }
-  // A window holding C - 1 tokens is full after this step's append; its group
-  // (the G oldest tokens) does not include the new one when R >= 1, so it is
-  // quantized first and the decode makes the page visible and appends.
-  ott::QuantizeList& due = h->due;
-  due.n = 0;
-  due.deferred = 1;
+  // A window holding C - 1 tokens is full after this step's append: its group
+  // (the G oldest tokens) is quantized and this step's decode makes the page
+  // visible. With R >= 1 the group never includes the new token, and it is
+  // complete as soon as the window holds G tokens, R - 1 steps or more before
+  // it is due: the quantize step may run any time in between, writing only
+  // what no decode reads yet (page nb, the other pool buffer) and reading what
+  // no append writes (the group's window slots, the live pool). So when some
+  // window is due and not quantized yet, one launch quantizes every window
+  // whose group is complete; the others' pages wait for their due steps.
   ott::StepArgs step{};
   step.k = static_cast<const __half*>(d_k);
   step.v = static_cast<const __half*>(d_v);
+  bool launch = false;
+  int n_due = 0;
   for (int b = 0; b < B; ++b) {
     if (h->rcnt[b] + 1 >= C) {
-      due.b[due.n++] = uint16_t(b);
+      ++n_due;
       step.adv[b >> 5] |= 1u << (b & 31);
+      launch |= !h->pending[b];
     }
   }
-  if (due.n > 0) {
-    st = after_launch(h, ott::launch_quantize(h->dev, due, static_cast<hipStream_t>(stream)));
+  if (launch) {
+    ott::QuantizeList& batch = h->due;
+    batch.n = 0;
+    batch.deferred = 1;
+    for (int b = 0; b < B; ++b)
+      if (h->rcnt[b] >= G && !h->pending[b]) batch.b[batch.n++] = uint16_t(b);
+    st = after_launch(h, ott::launch_quantize(h->dev, batch, static_cast<hipStream_t>(stream)));
     if (st != OTT_OK) return st;
+    for (int i = 0; i < batch.n; ++i) h->pending[batch.b[i]] = 1;
   }
-  // the host copy of the counters as the decode sees them (after the quantize
-  // step, before the append), then after the append
-  for (int i = 0; i < due.n; ++i) {
-    const int b = due.b[i];
-    h->head[b] = (h->head[b] + G) % C;
-    h->rcnt[b] -= G;
-    h->nb[b] += 1;
+  // the host copy of the counters as the decode sees them (the due pages
+  // visible, before the append), then after the append
+  for (int b = 0; b < B; ++b) {
+    if (h->rcnt[b] + 1 >= C) {
+      h->head[b] = (h->head[b] + G) % C;
+      h->rcnt[b] -= G;
+      h->nb[b] += 1;
+      h->pending[b] = 0;
+    }
   }
   st = launch_decode_planned(h, d_q, d_out, step, stream);
   for (int b = 0; b < B; ++b) {
     h->L[b] += 1;
     h->rcnt[b] += 1;
   }
-  if (st == OTT_OK && n_seq_quantized) *n_seq_quantized = due.n;
+  if (st == OTT_OK && n_seq_quantized) *n_seq_quantized = n_due;
   return st;
 }
 

@@ -22,6 +22,7 @@ struct Arena {
   uint64_t off_ring_k, off_ring_v, off_partials;
   float sm_scale;
   int32_t retention;  // pool rule: 0 smallest squared Key norm, 1 largest, 2 random per position
+  int32_t lds_max;    // dynamic LDS bytes a work-group may use on this device (0: unknown)
 };
 
 // New-token counts of one ott_append call and the window slot of each

@@ -129,18 +129,26 @@ struct QuantLds {
   int* wsum;      // [16] per-wave member counts of the group
 };
 
-// Dynamic LDS bytes of the QuantLds layout for (G, P).
-__host__ __device__ inline size_t quant_lds_bytes(int G, int P) {
+// Dynamic LDS bytes of the QuantLds layout for (G, P) with a stage of
+// `stage` rows (kStageRows, or 0 when the rows live in LDS whole).
+__host__ __device__ inline size_t quant_lds_bytes(int G, int P, int stage = kStageRows) {
   const size_t nc = size_t(P) + G;
-  return size_t(kStageRows) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
+  return size_t(stage) * D * 2 + (D + size_t(G)) * sizeof(CodeThr) +
          2 * size_t(kMinMaxParts) * D * sizeof(float) + nc * sizeof(double) + 4 * nc * sizeof(int) +
          G * sizeof(int) + 16 * sizeof(int);
 }
 
-__device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
+// LDS bytes of a quantize step that holds every candidate's K and V rows in
+// LDS ([P + G][D] each, after the QuantLds layout without a stage).
+__host__ __device__ inline size_t resident_lds_bytes(int G, int P) {
+  return ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15)) + 2 * (size_t(P) + G) * D * sizeof(__half);
+}
+
+__device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G,
+                                              int stage = kStageRows) {
   QuantLds q;
   q.stage = reinterpret_cast<__half*>(base);
-  q.kq = reinterpret_cast<CodeThr*>(base + kStageRows * D * sizeof(__half));
+  q.kq = reinterpret_cast<CodeThr*>(base + stage * D * sizeof(__half));
   q.vq = q.kq + D;
   q.klo = reinterpret_cast<float*>(q.vq + G);
   q.khi = q.klo + kMinMaxParts * D;
@@ -153,6 +161,22 @@ __device__ __forceinline__ QuantLds quant_lds(uint8_t* base, int NCmax, int G) {
   q.wsum = q.mem + G;
   return q;
 }
+
+// Where pack_page finds the members' rows. Staged: rows are read from global
+// memory through row functors (krow/vrow of a candidate's s.src) into the LDS
+// stage, kStageRows members at a time. Resident: every candidate's rows are
+// already in LDS, row i = candidate i (member t is candidate s.mem[t]).
+template <typename KRow, typename VRow>
+struct StagedRows {
+  static constexpr bool kResident = false;
+  KRow krow;
+  VRow vrow;
+};
+struct ResidentRows {
+  static constexpr bool kResident = true;
+  const __half* k;  // [candidates][D]
+  const __half* v;
+};
 
 // Copies rows [t0, t0+cnt) of the member list into the LDS stage with
 // independent 16-byte loads (one round trip for the whole chunk).
@@ -299,28 +323,42 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
 // Steps 4-6 of a quantize step: the page pg from its n_valid members (s.mem
 // in position order, rows krow(s.src[m]) and vrow(s.src[m])): Key (min, scale)
 // per channel and codes, Value (min, scale) per member and codes, zero padding.
-template <typename KRow, typename VRow>
+template <typename Rows>
 __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const QuantLds& s,
-                                          int n_valid, KRow krow, VRow vrow) {
+                                          int n_valid, const Rows& rows) {
   const int G = a.G;
   const int tid = threadIdx.x;
-  const int n_chunks = (n_valid + kStageRows - 1) / kStageRows;
+  // member rows: chunks of the stage, or one chunk of all members in LDS
+  constexpr bool kRes = Rows::kResident;
+  const int chunk_rows = kRes ? max(n_valid, 1) : kStageRows;
+  const int n_chunks = (n_valid + chunk_rows - 1) / chunk_rows;
+  // row of member t0 + t (t within the chunk starting at t0)
+  auto krow_of = [&](int t0, int t) -> const __half* {
+    if constexpr (kRes) return rows.k + size_t(s.mem[t0 + t]) * D;
+    else return s.stage + size_t(t) * D;
+  };
+  auto vrow_of = [&](int t0, int t) -> const __half* {
+    if constexpr (kRes) return rows.v + size_t(s.mem[t0 + t]) * D;
+    else return s.stage + size_t(t) * D;
+  };
   // 4. Key (min, scale) per channel over the members: kMinMaxParts partial
   //    scans per channel, then one thread per channel combines them
   {
     float lo = INFINITY, hi = -INFINITY;
     const int c = tid % D, part = tid / D;  // blockDim.x == kMinMaxParts * D
     for (int ch = 0; ch < n_chunks; ++ch) {
-      const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
-      stage_rows(s, t0, cnt, krow);
-      __syncthreads();
+      const int t0 = ch * chunk_rows, cnt = min(chunk_rows, n_valid - t0);
+      if constexpr (!kRes) {
+        stage_rows(s, t0, cnt, rows.krow);
+        __syncthreads();
+      }
 #pragma unroll 4
       for (int t = part; t < cnt; t += kMinMaxParts) {
-        const float x = __half2float(s.stage[t * D + c]);
+        const float x = __half2float(krow_of(t0, t)[c]);
         lo = fminf(lo, x);
         hi = fmaxf(hi, x);
       }
-      __syncthreads();
+      if constexpr (!kRes) __syncthreads();
     }
     s.klo[part * D + c] = lo;
     s.khi[part * D + c] = hi;
@@ -344,10 +382,12 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
   // 5. K codes, token-major: dword (t, j) = channels 16j..16j+15 of member t
   uint32_t* kc = reinterpret_cast<uint32_t*>(pg + kcode_off(G));
   for (int ch = 0; ch < n_chunks; ++ch) {
-    const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
-    if (n_chunks > 1) {  // a single chunk is still staged from step 4
-      stage_rows(s, t0, cnt, krow);
-      __syncthreads();
+    const int t0 = ch * chunk_rows, cnt = min(chunk_rows, n_valid - t0);
+    if constexpr (!kRes) {
+      if (n_chunks > 1) {  // a single chunk is still staged from step 4
+        stage_rows(s, t0, cnt, rows.krow);
+        __syncthreads();
+      }
     }
     const int jk = tid % (D / 16);  // this thread's 16 channels: 16*jk .. 16*jk+15
     CodeThr kq[16];  // the 8 blocks a wave reads for one cc are 128 contiguous bytes
@@ -355,7 +395,7 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
     for (int cc = 0; cc < 16; ++cc) kq[cc] = s.kq[cc * (D / 16) + jk];
     for (int w = tid; w < cnt * (D / 16); w += blockDim.x) {
       const int t = w / (D / 16), j = jk;
-      const uint4* row = reinterpret_cast<const uint4*>(s.stage + t * D + 16 * j);
+      const uint4* row = reinterpret_cast<const uint4*>(krow_of(t0, t) + 16 * j);
       const uint4 r0 = row[0], r1 = row[1];
       const uint32_t hw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
       uint32_t word = 0;
@@ -376,34 +416,39 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
   uint32_t* vmeta = reinterpret_cast<uint32_t*>(pg + vmeta_off(G));
   const int vdw = G / 16;
   for (int ch = 0; ch < n_chunks; ++ch) {
-    const int t0 = ch * kStageRows, cnt = min(kStageRows, n_valid - t0);
-    stage_rows(s, t0, cnt, vrow);
-    __syncthreads();
+    const int t0 = ch * chunk_rows, cnt = min(chunk_rows, n_valid - t0);
+    if constexpr (!kRes) {
+      stage_rows(s, t0, cnt, rows.vrow);
+      __syncthreads();
+    }
     {
       // 8 lanes per member, 16 channels each (rotated per member against bank
-      // conflicts), combined with cross-lane swaps inside the 8
-      const int t = tid >> 3, part = tid & 7;
-      float mn = INFINITY, mx = -INFINITY;
-      if (t < cnt) {
-        const __half* row = s.stage + t * D;
+      // conflicts), combined with cross-lane swaps inside the 8; blockDim / 8
+      // members per pass
+      for (int tb = 0; tb < cnt; tb += int(blockDim.x) / 8) {
+        const int t = tb + (tid >> 3), part = tid & 7;
+        float mn = INFINITY, mx = -INFINITY;
+        if (t < cnt) {
+          const __half* row = vrow_of(t0, t);
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
-          mn = fminf(mn, x);
-          mx = fmaxf(mx, x);
+          for (int i = 0; i < D / 8; ++i) {
+            const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+          }
         }
-      }
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-      }
-      if (t < cnt && part == 0) {
-        const uint32_t mn_b = meta_bits(mn);
-        const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
-        s.vq[t0 + t] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
-                                       __half2float(__ushort_as_half(uint16_t(sc_b))));
-        vmeta[t0 + t] = mn_b | (sc_b << 16);
+        for (int o = 1; o < 8; o <<= 1) {
+          mn = fminf(mn, __shfl_xor(mn, o));
+          mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        if (t < cnt && part == 0) {
+          const uint32_t mn_b = meta_bits(mn);
+          const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+          s.vq[t0 + t] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
+                                         __half2float(__ushort_as_half(uint16_t(sc_b))));
+          vmeta[t0 + t] = mn_b | (sc_b << 16);
+        }
       }
     }
     __syncthreads();
@@ -416,7 +461,7 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
       for (int cc = 0; cc < 16; ++cc) {
         const int t = 16 * j + cc;
         if (t < n_valid)
-          word |= qcode(__half2float(s.stage[(t - t0) * D + c]), s.vq[t]) << (2 * cc);
+          word |= qcode(__half2float(vrow_of(t0, t - t0)[c]), s.vq[t]) << (2 * cc);
       }
       vc[c * vdw + j] = word;
     }
@@ -434,6 +479,11 @@ __device__ __forceinline__ void pack_page(const Arena& a, uint8_t* pg, const Qua
 // (g_head + j) % g_mod of gk/gv (the window ring, or a prompt), competing with
 // the pool of buffer nb & 1; writes page nb, the new pool into the other
 // buffer and the page's member list. Counters are the caller's.
+// kResident: every candidate's K and V rows, and the pool's keys and
+// positions, are loaded into LDS first, all in one round trip, and every later
+// phase reads them there (resident_lds_bytes of LDS); otherwise the members'
+// rows are staged from global memory for the Key and the Value halves.
+template <bool kResident>
 __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
                                               const __half* __restrict__ gk,
                                               const __half* __restrict__ gv, int g_head,
@@ -445,7 +495,7 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
   const int npc = min(P, NC);
   const int n_valid = NC - npc;
   const int cur = nb & 1, nxt = cur ^ 1;
-  QuantLds s = quant_lds(lds_raw, P + G, G);
+  QuantLds s = quant_lds(lds_raw, P + G, G, kResident ? 0 : kStageRows);
 
   const __half* pk = pool_k(a, cur, bh);
   const __half* pv = pool_v(a, cur, bh);
@@ -455,8 +505,34 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
   auto vrow = [&](int src) -> const __half* {
     return (src & kRingFlag) ? gv + size_t(src & ~kRingFlag) * D : pv + size_t(src) * D;
   };
-  select_step(a, nb, pool_n2(a, cur, bh), pool_pos(a, cur, bh), gk, g_head, g_mod, s);
-  pack_page(a, page_ptr(a, bh, nb), s, n_valid, krow, vrow);
+  __half* kr = reinterpret_cast<__half*>(lds_raw + ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15)));
+  __half* vr = kr + size_t(P + G) * D;
+  if constexpr (kResident) {
+    // 0. candidate i's rows into LDS row i (pool entries, then the group), the
+    //    pool's keys and positions into the candidate arrays
+    const double* pkey = pool_n2(a, cur, bh);
+    const int32_t* ppos = pool_pos(a, cur, bh);
+    for (int x = tid; x < NC * (D / 8); x += blockDim.x) {
+      const int i = x / (D / 8), c8 = x % (D / 8);
+      const int row = i < pc ? i : (g_head + i - pc) % g_mod;
+      const __half* ks = (i < pc ? pk : gk) + size_t(row) * D;
+      const __half* vs = (i < pc ? pv : gv) + size_t(row) * D;
+      reinterpret_cast<uint4*>(kr + size_t(i) * D)[c8] = reinterpret_cast<const uint4*>(ks)[c8];
+      reinterpret_cast<uint4*>(vr + size_t(i) * D)[c8] = reinterpret_cast<const uint4*>(vs)[c8];
+    }
+    for (int i = tid; i < pc; i += blockDim.x) {
+      s.n2[i] = pkey[i];
+      s.pos[i] = ppos[i];
+    }
+    __syncthreads();
+    // 1-3 with the group's rows at LDS rows pc..pc+G-1
+    select_step(a, nb, s.n2, s.pos, kr + size_t(pc) * D, 0, G, s);
+    pack_page(a, page_ptr(a, bh, nb), s, n_valid, ResidentRows{kr, vr});
+  } else {
+    select_step(a, nb, pool_n2(a, cur, bh), pool_pos(a, cur, bh), gk, g_head, g_mod, s);
+    pack_page(a, page_ptr(a, bh, nb), s, n_valid,
+              StagedRows<decltype(krow), decltype(vrow)>{krow, vrow});
+  }
   // 8. the new pool, slot = rank, into the other buffer
   __half* nk = pool_k(a, nxt, bh);
   __half* nv = pool_v(a, nxt, bh);
@@ -464,10 +540,10 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
     const int i = w / (D / 8), c8 = w % (D / 8);
     const int r = s.rank[i];
     if (r < npc) {
-      reinterpret_cast<uint4*>(nk + size_t(r) * D)[c8] =
-          reinterpret_cast<const uint4*>(krow(s.src[i]))[c8];
-      reinterpret_cast<uint4*>(nv + size_t(r) * D)[c8] =
-          reinterpret_cast<const uint4*>(vrow(s.src[i]))[c8];
+      const __half* ks = kResident ? kr + size_t(i) * D : krow(s.src[i]);
+      const __half* vs = kResident ? vr + size_t(i) * D : vrow(s.src[i]);
+      reinterpret_cast<uint4*>(nk + size_t(r) * D)[c8] = reinterpret_cast<const uint4*>(ks)[c8];
+      reinterpret_cast<uint4*>(nv + size_t(r) * D)[c8] = reinterpret_cast<const uint4*>(vs)[c8];
       if (c8 == 0) {
         pool_pos(a, nxt, bh)[r] = s.pos[i];
         pool_n2(a, nxt, bh)[r] = s.n2[i];
@@ -483,6 +559,7 @@ __device__ __forceinline__ void quantize_step(const Arena& a, int bh, int nb,
   __syncthreads();
 }
 
+template <bool kResident>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, QuantizeList due) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const int h = blockIdx.x, b = due.b[blockIdx.y];
@@ -492,12 +569,12 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
     // a fused step: the host picked this sequence; the step's decode advances
     // the counters (it may be writing the window count and length meanwhile,
     // so only the window head and page count are read here)
-    quantize_step(a, bh, ctr[3], ring_k(a, bh), ring_v(a, bh), ctr[2], a.C, lds_raw);
+    quantize_step<kResident>(a, bh, ctr[3], ring_k(a, bh), ring_v(a, bh), ctr[2], a.C, lds_raw);
     return;
   }
   const int r_cnt = ctr[1], head = ctr[2], nb = ctr[3];
   if (r_cnt < a.C) return;  // window not full: nothing to do for this sequence
-  quantize_step(a, bh, nb, ring_k(a, bh), ring_v(a, bh), head, a.C, lds_raw);
+  quantize_step<kResident>(a, bh, nb, ring_k(a, bh), ring_v(a, bh), head, a.C, lds_raw);
   if (threadIdx.x == 0) {
     ctr[1] = r_cnt - a.G;
     ctr[2] = (head + a.G) % a.C;
@@ -633,7 +710,8 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_pack_kernel(
   __syncthreads();
   auto krow = [&](int pos) -> const __half* { return kb + size_t(pos) * D; };
   auto vrow = [&](int pos) -> const __half* { return vb + size_t(pos) * D; };
-  pack_page(a, page_ptr(a, bh, n), s, n_valid, krow, vrow);
+  pack_page(a, page_ptr(a, bh, n), s, n_valid,
+            StagedRows<decltype(krow), decltype(vrow)>{krow, vrow});
 }
 
 }  // namespace
@@ -680,13 +758,20 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
 
 hipError_t launch_quantize(const Arena& a, const QuantizeList& due, hipStream_t s) {
   dim3 grid(a.Hkv, due.n);
-  const size_t lds = quantize_lds_bytes(a.G, a.P);
-  if (lds > 65536) {  // the largest pools need more than the default dynamic LDS limit
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(quantize_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  // every candidate's rows resident in LDS when they fit the device's limit
+  const size_t lds_res = resident_lds_bytes(a.G, a.P);
+  const bool resident = a.lds_max > 0 && lds_res <= size_t(a.lds_max);
+  const size_t lds = resident ? lds_res : quantize_lds_bytes(a.G, a.P);
+  const void* fn = resident ? reinterpret_cast<const void*>(quantize_kernel<true>)
+                            : reinterpret_cast<const void*>(quantize_kernel<false>);
+  if (lds > 65536) {  // above the default dynamic LDS limit
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(quantize_kernel, grid, dim3(kQuantThreads), lds, s, a, due);
+  if (resident)
+    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(kQuantThreads), lds, s, a, due);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(kQuantThreads), lds, s, a, due);
   return hipGetLastError();
 }
 

@@ -211,12 +211,17 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
  *              OTT_ERR_INVALID_ARG. The k/v rows are copied into the window.
  *   *n_seq_quantized (may be NULL) receives the number of sequences whose group
  *   was quantized in this step.
- *   How: with R >= 1 a window holding R+G-1 tokens is quantized before the
- *   append (its G oldest tokens, the group, do not include the new one, so the
- *   result is the same); the decode then attends the new token from d_k/d_v and
- *   the head's single writer stores it in the window. One launch when no window
- *   fills (two with split-K), one more when one does. With R = 0 (the new token
- *   joins the group) or before any append/prefill, the three calls are made.
+ *   How: with R >= 1 the group a full window quantizes (its G oldest tokens)
+ *   never includes the new token and is complete once the window holds G
+ *   tokens, so its quantize step can run early: when a window is due and its
+ *   group not yet quantized, one launch quantizes every window whose group is
+ *   complete, writing only the next page and the other pool buffer, which no
+ *   decode reads until that window's due step; the due step's decode then makes
+ *   the page visible (the result is the same as quantizing at the due step).
+ *   The decode attends the new token from d_k/d_v and the head's single writer
+ *   stores it in the window. One launch per step (two with split-K), one more on
+ *   the steps that quantize. With R = 0 (the new token joins the group) or
+ *   before any append/prefill, the three calls are made.
  *   OTT_ERR_STATE if some window already holds R+G tokens (call
  *   ott_quantize_group first); OTT_ERR_CAPACITY if some L_b + 1 > max_seq_len.
  *   Nothing is enqueued on error.

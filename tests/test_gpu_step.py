@@ -51,10 +51,20 @@ def test_step_parameters(G, R, P, L, Hq, splits):
 
 def test_step_ragged_batch_many_quantizes():
     """Ragged lengths from 1 and 80 steps: every sequence crosses a quantize
-    step at its own step (some before any page exists)."""
+    step at its own step (some before any page exists); state after every step."""
     w = small("step-ragged", B=6, Hq=8, Hkv=2, G=64, R=16, P=8, L=(1, 1), steps=80)
     run_case(w, lengths=[1, 40, 79, 80, 200, 333], splits=[0, 3], step_calls="step",
-             state_every_step=False)
+             state_every_step=True)
+
+
+def test_step_quantizes_complete_groups_early():
+    """R = 48 > G / 2 with 8 sequences at spread phases: a window's group is
+    complete up to 47 steps before it is due, so a quantize launch covers
+    several windows, whose pages stay invisible until their due steps; the
+    state must match the oracle after every step."""
+    w = small("step-early", B=8, Hq=4, Hkv=2, G=64, R=48, P=16, L=(1, 1), steps=130, seed=9)
+    run_case(w, lengths=[500, 507, 514, 521, 530, 541, 552, 563], splits=[0],
+             step_calls="step", state_every_step=True)
 
 
 def test_step_mixed_with_separate_calls():
