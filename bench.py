@@ -38,7 +38,8 @@ HBM_PEAK_GBS = 8000.0
 MHA_SOURCES = ("decode_attention_ott_amd/csrc/ott_decode.hip",
                "decode_attention_ott_amd/csrc/ott_decode_common.h",
                "decode_attention_ott_amd/csrc/ott_mx.h",
-               "decode_attention_ott_amd/csrc/ott_device.h")
+               "decode_attention_ott_amd/csrc/ott_device.h",
+               "decode_attention_ott_amd/csrc/ott_kernels.h")
 GQA_SOURCES = MHA_SOURCES + ("decode_attention_ott_amd/csrc/ott_decode_gqa.hip",)
 
 

@@ -249,7 +249,8 @@ struct alignas(16) WaveLds {
 };
 
 // G <= 128 fits 128 VGPRs (4 waves per SIMD); G = 256 holds twice the codes.
-template <int G>
+// kStep: a fused step's decode (the new token, counter advances, the store).
+template <int G, bool kStep>
 __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, const __half* __restrict__ q,
                                                      __half* __restrict__ out, int S,
                                                      HeadOrder order, StepArgs step) {
@@ -262,15 +263,21 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);  // = b * H + h
   const int b = bh / a.Hkv;
 
-  const HeadCtr hc = head_counters(a, step, b, bh);
+  const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
   const int pc = min(a.P, a.G * nb);
-  const int n_new = step.k ? 1 : 0;  // a fused step's new token, after the window
+  const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
   const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
   const int p1 = sp.p1, t1 = sp.t1;
   const int buf = nb & 1;
-  const Fp16Src src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
-                    head, a.C, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
+  const Fp16Src base_src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
+                         head, a.C};
+  const auto src = [&] {
+    if constexpr (kStep)
+      return Fp16StepSrc{base_src, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
+    else
+      return base_src;
+  }();
   const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
         part[1] = Ls;
       }
     }
-  } else if (step.k && S == 1 && threadIdx.x < D + 32) {
+  } else if (kStep && S == 1 && threadIdx.x < D + 32) {
     // a fused step with one split: this work-group is the head's only reader
     // of its counters, so it stores the new token and the counters itself
     step_store(a, step, bh, hc, threadIdx.x - D);
@@ -379,9 +386,22 @@ __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict_
     const int NQ = a.Hq / a.Hkv, b = bq / a.Hq, qh = bq % a.Hq;
     if (qh % NQ == 0) {
       const int bh = b * a.Hkv + qh / NQ;
-      step_store(a, step, bh, head_counters(a, step, b, bh), threadIdx.x);
+      step_store(a, step, bh, head_counters<true>(a, step, b, bh), threadIdx.x);
     }
   }
+}
+
+template <bool kStep>
+hipError_t launch_g(const Arena& a, const __half* qh, __half* oh, int S, const HeadOrder& order,
+                    const StepArgs& step, hipStream_t s) {
+  const dim3 grid(unsigned(a.B) * a.Hkv * S);
+  switch (a.G) {
+    case 64: hipLaunchKernelGGL((decode_kernel<64, kStep>), grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
+    case 128: hipLaunchKernelGGL((decode_kernel<128, kStep>), grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
+    case 256: hipLaunchKernelGGL((decode_kernel<256, kStep>), grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -391,9 +411,9 @@ int decode_wgs_per_cu(const Arena& a) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (a.G) {
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<64>, 64 * kWaves, 0); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<128>, 64 * kWaves, 0); break;
-    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<256>, 64 * kWaves, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<64, false>, 64 * kWaves, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<128, false>, 64 * kWaves, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<256, false>, 64 * kWaves, 0); break;
     default: break;
   }
   return e == hipSuccess ? n : 0;
@@ -407,14 +427,8 @@ hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, const 
   if (a.Hq != a.Hkv) {
     e = launch_decode_gqa(a, q, out, S, order, step, s);
   } else {
-    const dim3 grid(unsigned(a.B) * a.Hkv * S);
-    switch (a.G) {
-      case 64: hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
-      case 128: hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
-      case 256: hipLaunchKernelGGL(decode_kernel<256>, grid, dim3(64 * kWaves), 0, s, a, qh, oh, S, order, step); break;
-      default: return hipErrorInvalidValue;
-    }
-    e = hipGetLastError();
+    e = step.k ? launch_g<true>(a, qh, oh, S, order, step, s)
+               : launch_g<false>(a, qh, oh, S, order, step, s);
   }
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(a.B) * a.Hq), dim3(D), 0, s, a, oh, S, step);

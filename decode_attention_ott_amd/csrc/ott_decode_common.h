@@ -156,28 +156,29 @@ __device__ __forceinline__ float quad_sum(float x) {
 // 16 lanes share one token (lane&15 takes channels 8*(lane&15)..+7), so every
 // load instruction reads 4 whole 256-byte rows. Scores reduce inside the row
 // with DPP; the row then holds the token's weight for its V accumulation.
-// In a fused step, token n_old (the last) is the step's new token, read from
-// the step's input rows nk/nv.
 struct Fp16Src {
   const __half* pk;
   const __half* pv;
   const __half* rk;
   const __half* rv;
   int pc, head, C;
-  int n_old;  // pool + window tokens
-  const __half* nk;
-  const __half* nv;
   __device__ __forceinline__ size_t row(int i) const {
     if (i < pc) return size_t(i) * D;
     const int x = head + i - pc;  // < 2C: head < C and i - pc < r_cnt <= C
     return size_t(x >= C ? x - C : x) * D;
   }
-  __device__ __forceinline__ const __half* k(int i) const {
-    return i >= n_old ? nk : (i < pc ? pk : rk) + row(i);
-  }
-  __device__ __forceinline__ const __half* v(int i) const {
-    return i >= n_old ? nv : (i < pc ? pv : rv) + row(i);
-  }
+  __device__ __forceinline__ const __half* k(int i) const { return (i < pc ? pk : rk) + row(i); }
+  __device__ __forceinline__ const __half* v(int i) const { return (i < pc ? pv : rv) + row(i); }
+};
+
+// The fp16 tokens of a fused step: token n_old (the last) is the step's new
+// token, read from the step's input rows nk/nv.
+struct Fp16StepSrc : Fp16Src {
+  int n_old;  // pool + window tokens
+  const __half* nk;
+  const __half* nv;
+  __device__ __forceinline__ const __half* k(int i) const { return i >= n_old ? nk : Fp16Src::k(i); }
+  __device__ __forceinline__ const __half* v(int i) const { return i >= n_old ? nv : Fp16Src::v(i); }
 };
 
 // Counters of (sequence, KV head) bh as a step's decode sees them: a quantize
@@ -189,8 +190,10 @@ struct HeadCtr {
 __device__ __forceinline__ bool step_adv(const StepArgs& st, int b) {
   return st.k != nullptr && ((st.adv[b >> 5] >> (b & 31)) & 1u);
 }
+template <bool kStep>
 __device__ __forceinline__ HeadCtr head_counters(const Arena& a, const StepArgs& st, int b, int bh) {
   const int32_t* ctr = counters(a, bh);
+  if constexpr (!kStep) return HeadCtr{0, ctr[1], ctr[2], ctr[3], false};
   HeadCtr c{ctr[0], ctr[1], ctr[2], ctr[3], step_adv(st, b)};
   if (c.adv) {
     c.r_cnt -= a.G;
@@ -231,7 +234,8 @@ struct Fp16Rows {
   uint4 k[kF16Pass], v[kF16Pass];
 };
 
-__device__ __forceinline__ void fp16_load(const Fp16Src& src, int base, int cnt, Fp16Rows& r,
+template <typename Src>
+__device__ __forceinline__ void fp16_load(const Src& src, int base, int cnt, Fp16Rows& r,
                                           int lane) {
   const int rw = lane >> 4, c8 = lane & 15;
   // rows past the chunk read the chunk's last token (in bounds); their
@@ -281,7 +285,8 @@ __device__ __forceinline__ void fp16_attend(const Fp16Rows& r, int cnt, const ui
   if (c8 == 0) st.l += lsum;  // each row's tokens counted once
 }
 
-__device__ __forceinline__ void fp16_chunk(const Fp16Src& src, int base, int cnt, const uint4& q8,
+template <typename Src>
+__device__ __forceinline__ void fp16_chunk(const Src& src, int base, int cnt, const uint4& q8,
                                            float qscale, Fp16State& st, int lane) {
   Fp16Rows r;
   fp16_load(src, base, cnt, r, lane);

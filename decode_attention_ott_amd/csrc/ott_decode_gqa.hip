@@ -314,7 +314,8 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
 // its state, then walks its pages (round-robin); the 4 wave states merge in
 // LDS. Heads past the KV head's last (a padded group) get a zero query and are
 // not written.
-template <int G, int NA>
+// kStep: a fused step's decode (the new token, counter advances, the store).
+template <int G, int NA, bool kStep>
 __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_gqa_kernel(
     Arena a, const __half* __restrict__ q, __half* __restrict__ out, int S, HeadOrder order,
     StepArgs step) {
@@ -330,14 +331,20 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
 
-  const HeadCtr hc = head_counters(a, step, b, bh);
+  const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
   const int pc = min(a.P, a.G * nb);
-  const int n_new = step.k ? 1 : 0;  // a fused step's new token, after the window
+  const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
   const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
   const int buf = nb & 1;
-  const Fp16Src src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
-                    head, a.C, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
+  const Fp16Src base_src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
+                         head, a.C};
+  const auto src = [&] {
+    if constexpr (kStep)
+      return Fp16StepSrc{base_src, pc + r_cnt, step.k + size_t(bh) * D, step.v + size_t(bh) * D};
+    else
+      return base_src;
+  }();
   const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   }
   // a fused step with one split: this work-group is the head's only reader of
   // its counters, so it stores the new token and the counters itself
-  if (step.k && S == 1 && threadIdx.x < 32) step_store(a, step, bh, hc, threadIdx.x);
+  if (kStep && S == 1 && threadIdx.x < 32) step_store(a, step, bh, hc, threadIdx.x);
 }
 
 template <int G>
@@ -486,10 +493,16 @@ hipError_t launch_g(const Arena& a, const __half* q, __half* out, int S, const H
                     const StepArgs& step, hipStream_t s) {
   const int NQ = a.Hq / a.Hkv;
   const dim3 grid(unsigned(a.B) * a.Hkv * S), block(64 * kWaves);
-  if (NQ % 8 == 0) {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, s, a, q, out, S, order, step);
+  if (step.k) {
+    if (NQ % 8 == 0)
+      hipLaunchKernelGGL((decode_gqa_kernel<G, 2, true>), grid, block, 0, s, a, q, out, S, order, step);
+    else
+      hipLaunchKernelGGL((decode_gqa_kernel<G, 1, true>), grid, block, 0, s, a, q, out, S, order, step);
   } else {
-    hipLaunchKernelGGL((decode_gqa_kernel<G, 1>), grid, block, 0, s, a, q, out, S, order, step);
+    if (NQ % 8 == 0)
+      hipLaunchKernelGGL((decode_gqa_kernel<G, 2, false>), grid, block, 0, s, a, q, out, S, order, step);
+    else
+      hipLaunchKernelGGL((decode_gqa_kernel<G, 1, false>), grid, block, 0, s, a, q, out, S, order, step);
   }
   return hipGetLastError();
 }
@@ -500,8 +513,8 @@ int wgs_g(const Arena& a) {
   int n = 0;
   const int bs = 64 * kWaves;
   const hipError_t e =
-      (NQ % 8 == 0) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 2>, bs, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 1>, bs, 0);
+      (NQ % 8 == 0) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 2, false>, bs, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_gqa_kernel<G, 1, false>, bs, 0);
   return e == hipSuccess ? n : 0;
 }
 
