@@ -265,6 +265,11 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
 
   const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
+  // a one-split fused step stores the new row at the end: load it now
+  uint4 piece{};
+  if constexpr (kStep)
+    if (S == 1 && threadIdx.x >= D && threadIdx.x < D + 32)
+      piece = step_row_piece(step, bh, threadIdx.x - D);
   const int pc = min(a.P, a.G * nb);
   const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
   const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   } else if (kStep && S == 1 && threadIdx.x < D + 32) {
     // a fused step with one split: this work-group is the head's only reader
     // of its counters, so it stores the new token and the counters itself
-    step_store(a, step, bh, hc, threadIdx.x - D);
+    step_store(a, bh, hc, threadIdx.x - D, piece);
   }
 }
 
@@ -381,14 +386,18 @@ __global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict_
   const int bq = blockIdx.x;  // b * Hq + qh
   const float* part = reinterpret_cast<const float*>(a.base + a.off_partials) +
                       size_t(bq) * a.max_splits * (2 + D);
-  out[size_t(bq) * D + threadIdx.x] = __float2half_rn(merge_partials(part, S, threadIdx.x));
-  if (step.k != nullptr && threadIdx.x < 32) {
-    const int NQ = a.Hq / a.Hkv, b = bq / a.Hq, qh = bq % a.Hq;
-    if (qh % NQ == 0) {
-      const int bh = b * a.Hkv + qh / NQ;
-      step_store(a, step, bh, head_counters<true>(a, step, b, bh), threadIdx.x);
-    }
+  // the step's store: its loads (counters, new row) go out with the partials'
+  const int NQ = a.Hq / a.Hkv, b = bq / a.Hq, qh = bq % a.Hq;
+  const int bh = b * a.Hkv + qh / NQ;
+  const bool writer = step.k != nullptr && qh % NQ == 0 && threadIdx.x < 32;
+  HeadCtr hc{};
+  uint4 piece{};
+  if (writer) {
+    hc = head_counters<true>(a, step, b, bh);
+    piece = step_row_piece(step, bh, threadIdx.x);
   }
+  out[size_t(bq) * D + threadIdx.x] = __float2half_rn(merge_partials(part, S, threadIdx.x));
+  if (writer) step_store(a, bh, hc, threadIdx.x, piece);
 }
 
 template <bool kStep>

@@ -204,17 +204,23 @@ __device__ __forceinline__ HeadCtr head_counters(const Arena& a, const StepArgs&
   return c;
 }
 
+// Lane t (0..31) of the head's single writer: its 16-byte piece of the
+// step's new K (t < 16) or V row of bh.
+__device__ __forceinline__ uint4 step_row_piece(const StepArgs& st, int bh, int t) {
+  return reinterpret_cast<const uint4*>((t < 16 ? st.k : st.v) + size_t(bh) * D)[t & 15];
+}
+
 // The step's new token of bh into window slot (head + r_cnt) % C, and the
-// head's counters; called by lanes t = 0..31 of the head's single writer.
-// The window head and page count are written only when they changed, so a
-// quantize step reading them elsewhere never races with this write.
-__device__ __forceinline__ void step_store(const Arena& a, const StepArgs& st, int bh,
-                                           const HeadCtr& c, int t) {
+// head's counters; called by lanes t = 0..31 of the head's single writer,
+// each with its piece of the row (step_row_piece). The window head and page
+// count are written only when they changed, so a quantize step reading them
+// elsewhere never races with this write.
+__device__ __forceinline__ void step_store(const Arena& a, int bh, const HeadCtr& c, int t,
+                                           const uint4& piece) {
   int slot = c.head + c.r_cnt;
   if (slot >= a.C) slot -= a.C;
-  const uint4* src = reinterpret_cast<const uint4*>((t < 16 ? st.k : st.v) + size_t(bh) * D);
   uint4* dst = reinterpret_cast<uint4*>((t < 16 ? ring_k(a, bh) : ring_v(a, bh)) + size_t(slot) * D);
-  dst[t & 15] = src[t & 15];
+  dst[t & 15] = piece;
   if (t == 0) {
     int32_t* ctr = counters(a, bh);
     ctr[0] = c.L + 1;

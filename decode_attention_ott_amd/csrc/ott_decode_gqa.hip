@@ -485,7 +485,8 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   }
   // a fused step with one split: this work-group is the head's only reader of
   // its counters, so it stores the new token and the counters itself
-  if (kStep && S == 1 && threadIdx.x < 32) step_store(a, step, bh, hc, threadIdx.x);
+  if (kStep && S == 1 && threadIdx.x < 32)
+    step_store(a, bh, hc, threadIdx.x, step_row_piece(step, bh, threadIdx.x));
 }
 
 template <int G>
