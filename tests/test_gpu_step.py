@@ -107,3 +107,18 @@ def test_step_from_a_fresh_handle_and_a_full_window():
     with pytest.raises(OttError, match="STATE"):
         layer.step(z, z, torch.zeros(2, 2, 128, dtype=torch.float16, device="cuda"))
     assert np.array_equal(layer.counters(), before)
+
+
+def _step_random_configs():
+    from tests.test_gpu_parity import _random_configs
+    return _random_configs(seed=4048)
+
+
+@pytest.mark.parametrize("case", _step_random_configs(), ids=lambda c: f"srand{c[0]}")
+def test_step_random_configurations(case):
+    """The seeded random configurations of the separate-call parity tests
+    (G, R from 0, P, heads, ratio, batch, ragged lengths from 1, step counts
+    across quantize steps, split counts), each step as one ott_step."""
+    i, G, R, P, Hkv, nq, B, lengths, steps, splits = case
+    w = synth.Workload(f"srand{i}", B, Hkv * nq, Hkv, 128, G, R, P, (1, 1), steps, seed=900 + i)
+    run_case(w, lengths=lengths, splits=splits, state_every_step=steps <= 16, step_calls="step")
