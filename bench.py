@@ -33,8 +33,8 @@ if ROOT not in sys.path:
 
 METRIC = "OTT decode-attention tokens/s + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
-# sources of the one-head decode kernel and the split combine; the grouped-head
-# kernel adds its own file
+# sources of the one-head decode kernel (its split merge included); the
+# grouped-head kernel adds its own file
 MHA_SOURCES = ("decode_attention_ott_amd/csrc/ott_decode.hip",
                "decode_attention_ott_amd/csrc/ott_decode_common.h",
                "decode_attention_ott_amd/csrc/ott_mx.h",
@@ -131,13 +131,15 @@ def staggered_lengths(w, lengths, n_states: int):
 
 
 def decode_kernel_name(w) -> str:
-    """The decode kernel a workload launches (the split combine kernel follows
-    it when a launch uses more than one split)."""
+    """The decode kernel a workload's decode-only loop launches, as rocprofv3
+    names it (with several splits, the last split of each head to finish merges
+    them inside the same launch; the fused step launches the same template with
+    `true`)."""
     nq = w.num_q_heads // w.num_kv_heads
     if nq == 1:
-        return f"decode_kernel<{w.group_size}>"
+        return f"decode_kernel<{w.group_size}, false>"
     na = 2 if nq % 8 == 0 else 1  # groups of 4 query heads per pass
-    return f"decode_gqa_kernel<{w.group_size}, {na}>"
+    return f"decode_gqa_kernel<{w.group_size}, {na}, false>"
 
 
 def decode_sources(w):

@@ -46,7 +46,7 @@ class ott_layout_t(ctypes.Structure):
                 ("off_pool_k", ctypes.c_uint64), ("off_pool_v", ctypes.c_uint64),
                 ("off_pool_pos", ctypes.c_uint64), ("off_pool_n2", ctypes.c_uint64),
                 ("off_ring_k", ctypes.c_uint64), ("off_ring_v", ctypes.c_uint64),
-                ("off_partials", ctypes.c_uint64)]
+                ("off_partials", ctypes.c_uint64), ("off_tickets", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -97,6 +97,7 @@ void fill_layout(const ott_config_t* c, ott_layout_t* L) {
   L->off_ring_k = take(BH * C * d * 2);
   L->off_ring_v = take(BH * C * d * 2);
   L->off_partials = take(B * Hq * uint64_t(L->max_splits) * (2 + d) * sizeof(float));
+  L->off_tickets = take(BH * sizeof(uint32_t));
   L->arena_bytes = off;
 }
 
@@ -214,6 +215,7 @@ ott_status_t ott_init(const ott_config_t* cfg, void* d_arena, size_t arena_bytes
   a.off_ring_k = lay.off_ring_k;
   a.off_ring_v = lay.off_ring_v;
   a.off_partials = lay.off_partials;
+  a.off_tickets = lay.off_tickets;
   a.sm_scale = h->cfg.sm_scale;
   a.retention = h->cfg.retention;
   const size_t nb = size_t(cfg->batch);

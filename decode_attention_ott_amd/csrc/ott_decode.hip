@@ -11,8 +11,9 @@
 //
 // A split is a byte-balanced slice of one (sequence, KV head)'s cache: a range
 // of pages and a range of fp16 tokens (pool first, then the window). With one
-// split the work-group writes the output; otherwise it writes its partial
-// state and a second kernel merges the splits.
+// split the work-group writes the output; otherwise every split writes its
+// partial state and takes a ticket, and the head's last split to arrive merges
+// all of them in the same launch (no second kernel, no launch gap).
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -256,6 +257,7 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
                                                      HeadOrder order, StepArgs step) {
   __shared__ WaveLds<G> lds_all[kWaves];
   __shared__ float mg_m[kWaves], mg_l[kWaves];
+  __shared__ uint32_t mg_last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   WaveLds<G>& L = lds_all[wave];
@@ -265,11 +267,11 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
 
   const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
-  // a one-split fused step stores the new row at the end: load it now
+  // a fused step's writer (the head's only or last split) stores the new row
+  // at the end: load it now
   uint4 piece{};
   if constexpr (kStep)
-    if (S == 1 && threadIdx.x >= D && threadIdx.x < D + 32)
-      piece = step_row_piece(step, bh, threadIdx.x - D);
+    if (threadIdx.x >= D && threadIdx.x < D + 32) piece = step_row_piece(step, bh, threadIdx.x - D);
   const int pc = min(a.P, a.G * nb);
   const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
   const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
@@ -365,10 +367,10 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
       out[size_t(bh) * D + c] = __float2half_rn(A / Ls);
     } else {
       float* part = partial_ptr(a, b, bh % a.Hq, s);
-      part[2 + c] = A;
+      st_coherent(part + 2 + c, A);
       if (c == 0) {
-        part[0] = M;
-        part[1] = Ls;
+        st_coherent(part, M);
+        st_coherent(part + 1, Ls);
       }
     }
   } else if (kStep && S == 1 && threadIdx.x < D + 32) {
@@ -376,28 +378,16 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
     // of its counters, so it stores the new token and the counters itself
     step_store(a, bh, hc, threadIdx.x - D, piece);
   }
-}
-
-// Merge of the S split partial states of each (sequence, query head). In a
-// fused step the work-group of each KV head's first query head also stores the
-// step's new token and the head's counters (every split has read them).
-__global__ __launch_bounds__(D) void combine_kernel(Arena a, __half* __restrict__ out, int S,
-                                                    StepArgs step) {
-  const int bq = blockIdx.x;  // b * Hq + qh
-  const float* part = reinterpret_cast<const float*>(a.base + a.off_partials) +
-                      size_t(bq) * a.max_splits * (2 + D);
-  // the step's store: its loads (counters, new row) go out with the partials'
-  const int NQ = a.Hq / a.Hkv, b = bq / a.Hq, qh = bq % a.Hq;
-  const int bh = b * a.Hkv + qh / NQ;
-  const bool writer = step.k != nullptr && qh % NQ == 0 && threadIdx.x < 32;
-  HeadCtr hc{};
-  uint4 piece{};
-  if (writer) {
-    hc = head_counters<true>(a, step, b, bh);
-    piece = step_row_piece(step, bh, threadIdx.x);
+  // several splits: the last one to finish merges them (every split has read
+  // the head's counters and window by then, so it is also the step's writer)
+  if (S > 1 && last_split(a, bh, S, &mg_last)) {
+    if (threadIdx.x < D)
+      out[size_t(bh) * D + threadIdx.x] =
+          __float2half_rn(merge_partials<true>(partial_ptr(a, b, bh % a.Hq, 0), S, threadIdx.x));
+    else if (kStep && threadIdx.x < D + 32)
+      step_store(a, bh, hc, threadIdx.x - D, piece);
+    if (threadIdx.x == 0) reset_ticket(a, bh);
   }
-  out[size_t(bq) * D + threadIdx.x] = __float2half_rn(merge_partials(part, S, threadIdx.x));
-  if (writer) step_store(a, bh, hc, threadIdx.x, piece);
 }
 
 template <bool kStep>
@@ -439,9 +429,7 @@ hipError_t launch_decode(const Arena& a, const void* q, void* out, int S, const 
     e = step.k ? launch_g<true>(a, qh, oh, S, order, step, s)
                : launch_g<false>(a, qh, oh, S, order, step, s);
   }
-  if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(a.B) * a.Hq), dim3(D), 0, s, a, oh, S, step);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace ott

@@ -322,11 +322,41 @@ __device__ __forceinline__ float* partial_ptr(const Arena& a, int b, int qh, int
          ((size_t(b) * a.Hq + qh) * a.max_splits + s) * (2 + D);
 }
 
+// Split-K partial states cross the XCDs: their L2 caches are not coherent
+// with each other for plain accesses, so the partials are written and read
+// with device-coherent (agent-scope) accesses, which reach the memory side
+// (the compiler's release and acquire fences would instead write back and drop
+// whole L2 contents at every split).
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K arrival, called by every thread of a work-group once its partial
+// states are written (st_coherent): true, in every thread, for the head's
+// last split to arrive, which then merges all S (ld_coherent). Each wave first
+// waits for its own partial stores to complete, so every split's partials are
+// in place before its ticket is taken. flag is LDS.
+__device__ __forceinline__ bool last_split(const Arena& a, int bh, int S, uint32_t* flag) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): loads and stores of this wave
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = (__hip_atomic_fetch_add(ticket(a, bh), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             uint32_t(S - 1)) ? 1u : 0u;
+  __syncthreads();
+  return *flag != 0u;
+}
+
 // Channel c of the merged output of S partial states {m, l, acc[D]} (log2
 // units) stored at part + s * (2 + D): the partials are read 16 at a time with
 // every load in flight, then merged online,
 // (M, L, A) <- (M', L e^(M-M') + sum l e^(m-M'), A e^(M-M') + sum acc e^(m-M')).
+template <bool kCoherent = false>
 __device__ __forceinline__ float merge_partials(const float* __restrict__ part, int S, int c) {
+  auto ld = [](const float* p) { return kCoherent ? ld_coherent(p) : *p; };
   constexpr int kChunk = 16;
   float M = -INFINITY, Ls = 0.f, A = 0.f;
   for (int i0 = 0; i0 < S; i0 += kChunk) {
@@ -335,9 +365,9 @@ __device__ __forceinline__ float merge_partials(const float* __restrict__ part, 
     for (int k = 0; k < kChunk; ++k) {
       const bool ok = i0 + k < S;
       const float* p = part + size_t(ok ? i0 + k : 0) * (2 + D);
-      m[k] = ok ? p[0] : -INFINITY;
-      l[k] = p[1];
-      v[k] = p[2 + c];
+      m[k] = ok ? ld(p) : -INFINITY;
+      l[k] = ld(p + 1);
+      v[k] = ld(p + 2 + c);
     }
     float Mc = M;
 #pragma unroll

@@ -322,6 +322,7 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   constexpr int QB = 4 * NA;
   __shared__ GxLds<G, NA> lds_all[kWaves];
   __shared__ float mg_m[kWaves][QB], mg_l[kWaves][QB];
+  __shared__ uint32_t mg_last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -474,19 +475,33 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
         out[(size_t(b) * a.Hq + qh) * D + c] = __float2half_rn(A / Ls);
       } else {
         float* part = partial_ptr(a, b, qh, s);
-        part[2 + c] = A;
+        st_coherent(part + 2 + c, A);
         if (c == 0) {
-          part[0] = M;
-          part[1] = Ls;
+          st_coherent(part, M);
+          st_coherent(part + 1, Ls);
         }
       }
     }
     __syncthreads();
   }
+  // a fused step's new row (its loads go out before the split arrival's wait)
+  uint4 piece{};
+  if (kStep && threadIdx.x < 32) piece = step_row_piece(step, bh, threadIdx.x);
   // a fused step with one split: this work-group is the head's only reader of
   // its counters, so it stores the new token and the counters itself
-  if (kStep && S == 1 && threadIdx.x < 32)
-    step_store(a, bh, hc, threadIdx.x, step_row_piece(step, bh, threadIdx.x));
+  if (kStep && S == 1 && threadIdx.x < 32) step_store(a, bh, hc, threadIdx.x, piece);
+  // several splits: the last one to finish merges them for every query head
+  // of the KV head (and is the step's writer: every split has read the
+  // counters and the window by then)
+  if (S > 1 && last_split(a, bh, S, &mg_last)) {
+    for (int x = threadIdx.x; x < NQ * D; x += blockDim.x) {
+      const int qh = hk * NQ + x / D, c = x % D;
+      out[(size_t(b) * a.Hq + qh) * D + c] =
+          __float2half_rn(merge_partials<true>(partial_ptr(a, b, qh, 0), S, c));
+    }
+    if (kStep && threadIdx.x < 32) step_store(a, bh, hc, threadIdx.x, piece);
+    if (threadIdx.x == 0) reset_ticket(a, bh);
+  }
 }
 
 template <int G>

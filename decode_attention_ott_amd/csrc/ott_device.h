@@ -20,6 +20,14 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int32_t* counters(const Arena& a, int bh) {
   return reinterpret_cast<int32_t*>(a.base + a.off_counters) + size_t(bh) * 4;
 }
+// splits of the running decode done with head bh (0 between launches); taken
+// and cleared with device-coherent atomics
+__device__ __forceinline__ uint32_t* ticket(const Arena& a, int bh) {
+  return reinterpret_cast<uint32_t*>(a.base + a.off_tickets) + bh;
+}
+__device__ __forceinline__ void reset_ticket(const Arena& a, int bh) {
+  __hip_atomic_store(ticket(a, bh), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint8_t* page_ptr(const Arena& a, int bh, int n) {
   return a.base + a.off_pages + (size_t(bh) * a.nb_max + n) * a.page_bytes;
 }

@@ -19,7 +19,7 @@ struct Arena {
   uint32_t page_bytes;
   uint64_t off_counters, off_pages, off_page_pos, off_page_nvalid;
   uint64_t off_pool_k, off_pool_v, off_pool_pos, off_pool_n2;
-  uint64_t off_ring_k, off_ring_v, off_partials;
+  uint64_t off_ring_k, off_ring_v, off_partials, off_tickets;
   float sm_scale;
   int32_t retention;  // pool rule: 0 smallest squared Key norm, 1 largest, 2 random per position
   int32_t lds_max;    // dynamic LDS bytes a work-group may use on this device (0: unknown)

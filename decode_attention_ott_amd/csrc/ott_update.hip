@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void append_kernel(Arena a, const uint4* __res
     ctr[1] = n;
     ctr[2] = 0;
     ctr[3] = 0;
+    reset_ticket(a, bh);
   }
   if (n == 0) return;
   uint4* rk = reinterpret_cast<uint4*>(ring_k(a, bh));
@@ -610,6 +611,7 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
     if (threadIdx.x == 0) {
       int32_t* ctr = counters(a, bh);
       ctr[0] = ctr[1] = ctr[2] = ctr[3] = 0;
+      reset_ticket(a, bh);
     }
     return;
   }
@@ -684,6 +686,7 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
     ctr[1] = rc;
     ctr[2] = head;
     ctr[3] = nq;
+    reset_ticket(a, bh);
   }
 }
 

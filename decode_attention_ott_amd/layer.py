@@ -171,6 +171,11 @@ class OTTLayer:
         n = self.B * self.Hkv * 4 * 4
         return self._region(self.layout.off_counters, n).view(np.int32).reshape(self.B, self.Hkv, 4)
 
+    def tickets(self) -> np.ndarray:
+        """uint32 [B, Hkv]: split arrivals of the running decode (0 between launches)."""
+        n = self.B * self.Hkv * 4
+        return self._region(self.layout.off_tickets, n).view(np.uint32).reshape(self.B, self.Hkv)
+
     def page_bytes(self, b: int, kvh: int, n: int) -> bytes:
         pb = self.layout.page_bytes
         bh = b * self.Hkv + kvh

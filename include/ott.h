@@ -105,7 +105,10 @@ enum { OTT_RETAIN_SMALLEST_NORM = 0, OTT_RETAIN_LARGEST_NORM = 1, OTT_RETAIN_RAN
  *   ring_k, ring_v   fp16  [B*Hkv][R+G][d]: the window; its r_cnt tokens sit in slots
  *              (ring_head + i) % (R+G), i = 0..r_cnt-1, at positions G*nb + i.
  *   partials   fp32  [B][Hq][max_splits][2+d]: split-K partial softmax states {m, l, acc[d]}
- *              (written by a split decode, read by the kernel that merges the splits).
+ *              (written by the splits of a decode, read by the split that merges them).
+ *   tickets    uint32 [B*Hkv]: splits of the running decode done with each (sequence, KV
+ *              head); 0 between launches (the merging split resets it; the first append or
+ *              prefill on the handle writes the 0).
  * No region needs to be cleared by the caller: every byte a kernel reads was
  * written earlier by one of this handle's kernels.
  */
@@ -127,6 +130,7 @@ typedef struct {
   uint64_t off_ring_k;
   uint64_t off_ring_v;
   uint64_t off_partials;
+  uint64_t off_tickets;
 } ott_layout_t;
 
 /*

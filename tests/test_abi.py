@@ -53,7 +53,7 @@ def test_sizing_matches_layout_formula():
     want = (al(B * Hkv * 16) + al(B * Hkv * NB * page) + al(B * Hkv * NB * G * 4)
             + al(B * Hkv * NB * 4) + 2 * al(2 * B * Hkv * P * d * 2) + al(2 * B * Hkv * P * 4)
             + al(2 * B * Hkv * P * 8) + 2 * al(B * Hkv * (R + G) * d * 2)
-            + al(B * Hq * S * (2 + d) * 4))
+            + al(B * Hq * S * (2 + d) * 4) + al(B * Hkv * 4))
     assert req == want
 
 

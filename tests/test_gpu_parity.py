@@ -169,19 +169,25 @@ def test_outlier_heavy_keys():
              state_every_step=True)
 
 
-def test_decode_is_deterministic_and_repeatable():
+@pytest.mark.parametrize("hq", [8, 2])
+def test_decode_is_deterministic_and_repeatable(hq):
+    # the last split to arrive merges, in split order, whichever split it is;
+    # every head's arrival ticket is back at 0 after each launch
     import torch
     from decode_attention_ott_amd import OTTLayer
-    w = small("det", B=2, Hq=8, Hkv=2, L=(1200, 1200))
+    w = small("det", B=2, Hq=hq, Hkv=2, L=(1200, 1200))
     K, V = synth.kv_all(w, 1200)
     layer = OTTLayer.for_workload(w, max_seq_len=1300)
     layer.prefill(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), [1200, 1200])
+    assert not layer.tickets().any()
     q = torch.from_numpy(synth.queries(w, 0)).cuda()
     outs = []
-    for s in (0, 0, 5, 5):
+    for s in (0, 0, 5, 5, 3, 1, 5):
         layer.set_num_splits(s)
         outs.append(layer.decode(q).cpu().numpy().view(np.uint16))
+        assert not layer.tickets().any(), s
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[2], outs[3])
+    assert np.array_equal(outs[2], outs[6])
 
 
 def test_capacity_error_leaves_state_unchanged():
@@ -190,6 +196,7 @@ def test_capacity_error_leaves_state_unchanged():
     layer = OTTLayer(1, 1, 1, 128, 128, 32, 32, max_seq_len=400)
     k = torch.zeros(1, 1, 160, 128, dtype=torch.float16, device="cuda")
     layer.append(k, k)
+    assert not layer.tickets().any()  # the first append clears them with the counters
     before = layer.counters().copy()
     with pytest.raises(OttError, match="CAPACITY"):
         layer.append(k[:, :, :1].contiguous(), k[:, :, :1].contiguous())
