@@ -350,41 +350,69 @@ __device__ __forceinline__ bool last_split(const Arena& a, int bh, int S, uint32
   return *flag != 0u;
 }
 
-// Channel c of the merged output of S partial states {m, l, acc[D]} (log2
-// units) stored at part + s * (2 + D): the partials are read 16 at a time with
-// every load in flight, then merged online,
+// Channels c[n] of the merged outputs of N sets of S partial states
+// {m, l, acc[D]} (log2 units), set n stored at part[n] + s * (2 + D): the
+// partials are read 16 splits at a time with every load of all N sets in
+// flight, then merged online,
 // (M, L, A) <- (M', L e^(M-M') + sum l e^(m-M'), A e^(M-M') + sum acc e^(m-M')).
-template <bool kCoherent = false>
-__device__ __forceinline__ float merge_partials(const float* __restrict__ part, int S, int c) {
+template <bool kCoherent, int N>
+__device__ __forceinline__ void merge_partials_n(const float* const (&part)[N], int S,
+                                                 const int (&c)[N], float (&out)[N]) {
   auto ld = [](const float* p) { return kCoherent ? ld_coherent(p) : *p; };
   constexpr int kChunk = 16;
-  float M = -INFINITY, Ls = 0.f, A = 0.f;
-  for (int i0 = 0; i0 < S; i0 += kChunk) {
-    float m[kChunk], l[kChunk], v[kChunk];
+  float M[N], Ls[N], A[N];
 #pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const bool ok = i0 + k < S;
-      const float* p = part + size_t(ok ? i0 + k : 0) * (2 + D);
-      m[k] = ok ? ld(p) : -INFINITY;
-      l[k] = ld(p + 1);
-      v[k] = ld(p + 2 + c);
-    }
-    float Mc = M;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[k]);
-    if (Mc == -INFINITY) continue;
-    const float f0 = (M == -INFINITY) ? 0.f : exp2f(M - Mc);
-    Ls *= f0;
-    A *= f0;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      const float f = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mc);
-      Ls = fmaf(l[k], f, Ls);
-      A = fmaf(v[k], f, A);
-    }
-    M = Mc;
+  for (int n = 0; n < N; ++n) {
+    M[n] = -INFINITY;
+    Ls[n] = 0.f;
+    A[n] = 0.f;
   }
-  return A / Ls;
+  for (int i0 = 0; i0 < S; i0 += kChunk) {
+    float m[N][kChunk], l[N][kChunk], v[N][kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k)
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        m[n][k] = -INFINITY;
+        l[n][k] = 0.f;
+        v[n][k] = 0.f;
+        if (i0 + k < S) {  // uniform
+          const float* p = part[n] + size_t(i0 + k) * (2 + D);
+          m[n][k] = ld(p);
+          l[n][k] = ld(p + 1);
+          v[n][k] = ld(p + 2 + c[n]);
+        }
+      }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float Mc = M[n];
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) Mc = fmaxf(Mc, m[n][k]);
+      if (Mc == -INFINITY) continue;
+      const float f0 = (M[n] == -INFINITY) ? 0.f : exp2f(M[n] - Mc);
+      Ls[n] *= f0;
+      A[n] *= f0;
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const float f = (m[n][k] == -INFINITY) ? 0.f : exp2f(m[n][k] - Mc);
+        Ls[n] = fmaf(l[n][k], f, Ls[n]);
+        A[n] = fmaf(v[n][k], f, A[n]);
+      }
+      M[n] = Mc;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) out[n] = A[n] / Ls[n];
+}
+
+// Channel c of the merged output of the S partial states at part.
+template <bool kCoherent = false>
+__device__ __forceinline__ float merge_partials(const float* part, int S, int c) {
+  const float* const ps[1] = {part};
+  const int cs[1] = {c};
+  float o[1];
+  merge_partials_n<kCoherent, 1>(ps, S, cs, o);
+  return o[0];
 }
 
 }  // namespace dec

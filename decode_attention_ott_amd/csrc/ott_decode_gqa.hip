@@ -494,10 +494,17 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   // of the KV head (and is the step's writer: every split has read the
   // counters and the window by then)
   if (S > 1 && last_split(a, bh, S, &mg_last)) {
-    for (int x = threadIdx.x; x < NQ * D; x += blockDim.x) {
-      const int qh = hk * NQ + x / D, c = x % D;
-      out[(size_t(b) * a.Hq + qh) * D + c] =
-          __float2half_rn(merge_partials<true>(partial_ptr(a, b, qh, 0), S, c));
+    // two outputs per thread and round, their loads in flight together
+    constexpr int kT = 64 * kWaves;
+    for (int x = threadIdx.x; x < NQ * D; x += 2 * kT) {
+      const int x1 = min(x + kT, NQ * D - 1);  // (a repeat of x's row when past the end)
+      const float* const ps[2] = {partial_ptr(a, b, hk * NQ + x / D, 0),
+                                  partial_ptr(a, b, hk * NQ + x1 / D, 0)};
+      const int cs[2] = {x % D, x1 % D};
+      float o[2];
+      merge_partials_n<true, 2>(ps, S, cs, o);
+      out[(size_t(b) * a.Hq + hk * NQ) * D + x] = __float2half_rn(o[0]);
+      if (x + kT < NQ * D) out[(size_t(b) * a.Hq + hk * NQ) * D + x1] = __float2half_rn(o[1]);
     }
     if (kStep && threadIdx.x < 32) step_store(a, bh, hc, threadIdx.x, piece);
     if (threadIdx.x == 0) reset_ticket(a, bh);
