@@ -72,8 +72,17 @@ def test_grouped_query_parameters(G, R, P, L, Hq):
 
 
 def test_grouped_query_split_counts_agree():
+    # past 16 splits the merge reads its partials in two rounds; at 64 most
+    # splits of a 16-page head are empty
     w = small("gqa-splits", B=2, Hq=8, Hkv=2, L=(2000, 2000), steps=2)
-    run_case(w, splits=[1, 2, 3, 7, 16, 0])
+    run_case(w, splits=[1, 2, 3, 7, 16, 17, 33, 64, 0])
+
+
+def test_grouped_query_merge_rounds():
+    # 6 query heads per KV head: the merging split's 256 threads take 768
+    # outputs in two rounds of two, the second pair half past the end
+    w = small("gqa-rounds", B=2, Hq=12, Hkv=2, L=(1500, 1500), steps=2)
+    run_case(w, splits=[5, 20])
 
 
 def test_grouped_query_huge_keys():
@@ -100,7 +109,7 @@ def test_one_split_head_orders():
 
 def test_split_counts_agree():
     w = small("splits", B=2, Hq=2, Hkv=2, L=(2000, 2000), steps=3)
-    run_case(w, splits=[1, 2, 3, 7, 16, 0])
+    run_case(w, splits=[1, 2, 3, 7, 16, 17, 40, 64, 0])
 
 
 @pytest.mark.parametrize("Hq", [2, 8])
