@@ -200,7 +200,9 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
  *   window, with one softmax over all of them.
  *   d_q   : device fp16 [B][Hq][d];  d_out : device fp16 [B][Hq][d]; both 16-byte
  *           aligned (else OTT_ERR_INVALID_ARG).
- *   The state is not modified; the call can be repeated.
+ *   The state is not modified; the call can be repeated. One launch: with
+ *   split-K (ott_set_num_splits) the last split of each head to finish merges
+ *   the partial states in split order, so results do not depend on timing.
  *   OTT_ERR_STATE if some sequence holds no token.
  */
 ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream);
@@ -223,8 +225,8 @@ ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stre
  *   decode reads until that window's due step; the due step's decode then makes
  *   the page visible (the result is the same as quantizing at the due step).
  *   The decode attends the new token from d_k/d_v and the head's single writer
- *   stores it in the window. One launch per step (two with split-K), one more on
- *   the steps that quantize. With R = 0 (the new token joins the group) or
+ *   (its only split, or its last split to finish) stores it in the window. One
+ *   launch per step, one more on the steps that quantize. With R = 0 (the new token joins the group) or
  *   before any append/prefill, the three calls are made.
  *   OTT_ERR_STATE if some window already holds R+G tokens (call
  *   ott_quantize_group first); OTT_ERR_CAPACITY if some L_b + 1 > max_seq_len.
