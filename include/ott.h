@@ -203,6 +203,8 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
  *   The state is not modified; the call can be repeated. One launch: with
  *   split-K (ott_set_num_splits) the last split of each head to finish merges
  *   the partial states in split order, so results do not depend on timing.
+ *   Two decodes of one handle must not overlap in time (they share the arena's
+ *   partials and tickets): order their streams like any other calls.
  *   OTT_ERR_STATE if some sequence holds no token.
  */
 ott_status_t ott_decode(ott_handle_t h, const void* d_q, void* d_out, void* stream);
