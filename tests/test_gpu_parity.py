@@ -199,6 +199,28 @@ def test_decode_is_deterministic_and_repeatable(hq):
     assert np.array_equal(outs[2], outs[6])
 
 
+@pytest.mark.parametrize("hq,splits", [(8, 12), (2, 19)])
+def test_split_merge_is_identical_over_many_launches(hq, splits):
+    # the merging split reads the other splits' partials through device-coherent
+    # loads after their ticket increments: 400 back-to-back launches, whose
+    # splits finish in a different order each time, give bit-identical outputs
+    import torch
+    from decode_attention_ott_amd import OTTLayer
+    w = small("merge-repeat", B=4, Hq=hq, Hkv=2, L=(6000, 6000))
+    K, V = synth.kv_all(w, 6000)
+    layer = OTTLayer.for_workload(w, max_seq_len=6100)
+    layer.prefill(torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), [6000] * 4)
+    layer.set_num_splits(splits)
+    q = torch.from_numpy(synth.queries(w, 0)).cuda()
+    first = layer.decode(q).clone()
+    outs = torch.empty((400,) + tuple(first.shape), dtype=first.dtype, device=first.device)
+    for i in range(400):
+        layer.decode(q, out=outs[i])
+    same = (outs.view(torch.int16) == first.view(torch.int16)).flatten(1).all(dim=1)
+    assert bool(same.all()), f"launches differing from the first: {(~same).nonzero().flatten().tolist()[:10]}"
+    assert not layer.tickets().any()
+
+
 def test_capacity_error_leaves_state_unchanged():
     import torch
     from decode_attention_ott_amd import OTTLayer, OttError
