@@ -190,13 +190,36 @@ __device__ __forceinline__ void stage_rows(const QuantLds& s, int t0, int cnt, R
   }
 }
 
+// Squared Key norm of one fp16 row: fp64, summed in channel order 0..D-1.
+__device__ __forceinline__ double sq_norm_fp64(const __half* __restrict__ k_row) {
+  const uint4* row = reinterpret_cast<const uint4*>(k_row);
+  uint4 w[D / 8];
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) w[c8] = row[c8];
+  double acc = 0.0;
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) {
+    const uint32_t ws[4] = {w[c8].x, w[c8].y, w[c8].z, w[c8].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double lo = double(__half2float(__ushort_as_half(uint16_t(ws[e] & 0xffffu))));
+      const double hi = double(__half2float(__ushort_as_half(uint16_t(ws[e] >> 16))));
+      acc = acc + lo * lo;
+      acc = acc + hi * hi;
+    }
+  }
+  return acc;
+}
+
 // Steps 1-3 of a quantize step for page nb: candidates (the pool's keys and
 // positions from pkey/ppos, then the group's G tokens, rows (g_head + j) %
 // g_mod of gk), their retention keys, ranks and the members in position order,
-// all in LDS (s). The caller finishes the step.
+// all in LDS (s). The caller finishes the step. pre_n2, when given, holds the
+// group tokens' squared norms (sq_norm_fp64 of their rows), computed earlier.
 __device__ __forceinline__ void select_step(const Arena& a, int nb, const double* pkey,
                                             const int32_t* ppos, const __half* __restrict__ gk,
-                                            int g_head, int g_mod, const QuantLds& s) {
+                                            int g_head, int g_mod, const QuantLds& s,
+                                            const double* __restrict__ pre_n2 = nullptr) {
   const int G = a.G, P = a.P;
   const int tid = threadIdx.x;
   const int pc = min(P, G * nb);  // pool tokens before this step
@@ -212,22 +235,7 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
     } else {
       const int j = i - pc;
       const int slot = (g_head + j) % g_mod;
-      const uint4* row = reinterpret_cast<const uint4*>(gk + size_t(slot) * D);
-      uint4 w[D / 8];
-#pragma unroll
-      for (int c8 = 0; c8 < D / 8; ++c8) w[c8] = row[c8];
-      double acc = 0.0;
-#pragma unroll
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        const uint32_t ws[4] = {w[c8].x, w[c8].y, w[c8].z, w[c8].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double lo = double(__half2float(__ushort_as_half(uint16_t(ws[e] & 0xffffu))));
-          const double hi = double(__half2float(__ushort_as_half(uint16_t(ws[e] >> 16))));
-          acc = acc + lo * lo;
-          acc = acc + hi * hi;
-        }
-      }
+      const double acc = pre_n2 ? pre_n2[j] : sq_norm_fp64(gk + size_t(slot) * D);
       s.n2[i] = retention_key(acc, G * nb + j, a.retention);
       s.pos[i] = G * nb + j;
       s.src[i] = slot | kRingFlag;
@@ -600,6 +608,23 @@ __device__ __forceinline__ int prefill_pages(const Arena& a, int L) {
   return L >= a.R + a.G ? (L - a.R) / a.G : 0;
 }
 
+// The squared Key norms of every group token of the prompt, all pages of all
+// heads at once: page n's G norms go to the first 8 G bytes of page n's own
+// slot, which prefill_pack_kernel overwrites with the page afterwards.
+__device__ __forceinline__ double* prefill_norms(const Arena& a, int bh, int n) {
+  return reinterpret_cast<double*>(page_ptr(a, bh, n));
+}
+
+__global__ __launch_bounds__(256) void prefill_norms_kernel(Arena a, const __half* __restrict__ k,
+                                                            int64_t max_len, PrefillLens lens) {
+  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.Hkv + h;
+  if (n >= prefill_pages(a, lens.len[b])) return;
+  const __half* kb = k + (size_t(bh) * max_len + size_t(n) * a.G) * D;
+  double* out = prefill_norms(a, bh, n);
+  for (int j = threadIdx.x; j < a.G; j += blockDim.x) out[j] = sq_norm_fp64(kb + size_t(j) * D);
+}
+
 __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
     PrefillLens lens) {
@@ -636,7 +661,8 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
   for (int n = 0; n < nq; ++n) {
     const int pc = min(P, G * n), NC = pc + G, npc = min(P, NC), n_valid = NC - npc;
     const int cur = n & 1;
-    select_step(a, n, pkey[cur], ppos[cur], kb + size_t(n) * G * D, 0, G, s);
+    select_step(a, n, pkey[cur], ppos[cur], kb + size_t(n) * G * D, 0, G, s,
+                prefill_norms(a, bh, n));
     int32_t* pp = page_pos_all + (size_t(bh) * a.nb_max + n) * G;
     for (int t = tid; t < G; t += blockDim.x) pp[t] = t < n_valid ? s.pos[s.mem[t]] : -1;
     if (tid == 0) page_nv_all[size_t(bh) * a.nb_max + n] = n_valid;
@@ -750,6 +776,12 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
   }
   const __half* kh = static_cast<const __half*>(k);
   const __half* vh = static_cast<const __half*>(v);
+  if (max_pages > 0) {
+    hipLaunchKernelGGL(prefill_norms_kernel, dim3(max_pages, a.Hkv, a.B), dim3(256), 0, s, a, kh,
+                       max_len, lens);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(prefill_select_kernel, dim3(a.Hkv, a.B), dim3(kQuantThreads), lds_sel, s, a,
                      kh, vh, max_len, lens);
   hipError_t e = hipGetLastError();
