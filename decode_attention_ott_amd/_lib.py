@@ -52,6 +52,18 @@ class ott_layout_t(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+def _one_hip_runtime() -> None:
+    """PyTorch ships its own HIP runtime (libamdhip64, libhsa-runtime64) under the
+    same sonames as the system ROCm copies that libott.so is linked against.
+    Imported first, torch's copies are in the process and libott.so binds to
+    them; loaded first, libott.so would map the system copies and torch its own,
+    and two HIP runtimes initialising the same GPU crash at the first GPU call."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # no torch: libott.so brings the system runtime alone
+        pass
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -92,6 +104,7 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
+_one_hip_runtime()
 lib = _load()
 
 

@@ -153,3 +153,20 @@ def test_init_enqueues_nothing_and_host_counts_are_checked():
         assert lay.arena_bytes == need and lay.off_partials < need
     finally:
         L.ott_destroy(h)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # the binding imported before torch must not map a second HIP runtime
+    # (torch's copy and the system copy share their sonames)
+    import subprocess
+    import sys
+    code = ("import decode_attention_ott_amd, torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps')"
+            " if 'libamdhip64' in l or 'libhsa-runtime64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    hip = [x for x in libs if "libamdhip64" in x]
+    hsa = [x for x in libs if "libhsa-runtime64" in x]
+    assert len(hip) == 1 and len(hsa) == 1, libs
