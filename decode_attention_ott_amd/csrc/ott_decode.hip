@@ -137,7 +137,7 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
   constexpr int NZ = P::NZ, NB = P::NB;
   const int j = lane & 15, g = lane >> 4;
   // ---- scores: q'_c = q_c scale_c as digits, bias = sum_c q_c min_c
-  const float qp0 = qs0 * hi_f(r.km[0]), qp1 = qs1 * hi_f(r.km[1]);
+  const float qp0 = mul_hi_f(qs0, r.km[0]), qp1 = mul_hi_f(qs1, r.km[1]);
   const float bias = wave_sum(fmaf(qs0, lo_f(r.km[0]), qs1 * lo_f(r.km[1])));
   const int eq = mx_exp(wave_max(fmaxf(fabsf(qp0), fabsf(qp1))));
   {
@@ -183,7 +183,7 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
     const float p = exp2_fast(z[i] - st.m);
     st.l += p;
     st.vmin = fmaf(p, lo_f(r.vm[i]), st.vmin);
-    pp[i] = p * hi_f(r.vm[i]);
+    pp[i] = mul_hi_f(p, r.vm[i]);
     pmax = fmaxf(pmax, pp[i]);
   }
   const int ep = mx_exp(wave_max(pmax));

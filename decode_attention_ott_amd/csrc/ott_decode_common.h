@@ -85,6 +85,12 @@ __device__ __forceinline__ float lo_f(uint32_t w) {
 __device__ __forceinline__ float hi_f(uint32_t w) {
   return __half2float(__ushort_as_half(uint16_t(w >> 16)));
 }
+// x times the fp16 value in the high half of w: one mixed-precision FMA with a
+// zero addend, the product rounded once as by a conversion and a multiply
+// (only the sign of a zero product may differ).
+__device__ __forceinline__ float mul_hi_f(float x, uint32_t w) {
+  return __builtin_fmaf(x, hi_f(w), 0.0f);
+}
 __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
                                 false);

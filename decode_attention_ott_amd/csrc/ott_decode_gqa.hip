@@ -161,13 +161,9 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
   const int j = lane & 15, g = lane >> 4;
 
   // ---- q' = qs scale_c for head g of each group, channels 8j..8j+7, as digits
-  float scl[8], mnv[8];
+  float mnv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t w = dw(r.km[i >> 2], i & 3);
-    mnv[i] = lo_f(w);
-    scl[i] = hi_f(w);
-  }
+  for (int i = 0; i < 8; ++i) mnv[i] = lo_f(dw(r.km[i >> 2], i & 3));
   // channel 8j + i sits at logical k = base + (i >> 1) + 8 (i & 1)
   const int base = 32 * (j >> 2) + 16 * ((j >> 1) & 1) + 4 * (j & 1);
   float bias[NA];
@@ -177,7 +173,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
     float qp[8], b = 0.f, amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      qp[i] = qs[a][i] * scl[i];
+      qp[i] = mul_hi_f(qs[a][i], dw(r.km[i >> 2], i & 3));
       b = fmaf(qs[a][i], mnv[i], b);
       amax = fmaxf(amax, fabsf(qp[i]));
     }
@@ -264,7 +260,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
       const float p = exp2_fast(z[a][T] - mref);
       st.l[a] += p;
       st.vmin[a] = fmaf(p, lo_f(r.vm[T]), st.vmin[a]);
-      pp[T] = p * hi_f(r.vm[T]);
+      pp[T] = mul_hi_f(p, r.vm[T]);
       pmax = fmaxf(pmax, pp[T]);
     }
     const int ep = mx_exp(row_max(pmax));
