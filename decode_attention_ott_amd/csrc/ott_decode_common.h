@@ -46,6 +46,29 @@ __device__ __forceinline__ float row_max(float x) {
   x = fmaxf(x, dpp<kRowMirror>(x));
   return x;
 }
+// Row maxima compared as unsigned integers: a float's bits with the sign bit
+// flipped (all bits when negative) order like the float (no NaN), and
+// non-negative floats order like their bits. An unsigned maximum folds into
+// its DPP move (0 is its identity), one instruction per step; a float maximum
+// of a moved value first quiets its input, four instructions per step.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kQuadSwap1, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kQuadSwap2, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kHalfMirror, 0xF, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kRowMirror, 0xF, 0xF, false)));
+  return v;
+}
+// x >= 0 (or -0) in every lane
+__device__ __forceinline__ float row_max_nonneg(float x) {
+  return __uint_as_float(row_max_u32(__float_as_uint(x) & 0x7fffffffu));
+}
+// any x but NaN
+__device__ __forceinline__ float row_max_ordered(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t u = row_max_u32(b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u));
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+
 // combine each lane with its partner row (lane ^ 16) / partner half (lane ^ 32)
 __device__ __forceinline__ f32x2 swap16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),

@@ -178,7 +178,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
       amax = fmaxf(amax, fabsf(qp[i]));
     }
     bias[a] = row_sum(b);
-    const int eq = mx_exp(row_max(amax));
+    const int eq = mx_exp(row_max_nonneg(amax));
     // digit rows one at a time (see mx_digits): r holds what is left
 #pragma unroll
     for (int i = 0; i < 8; ++i) qp[i] = __builtin_amdgcn_ldexpf(qp[i], 4 - eq);
@@ -234,7 +234,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
     float mx = z[a][0];
 #pragma unroll
     for (int T = 1; T < NT; ++T) mx = fmaxf(mx, z[a][T]);
-    mx = row_max(mx);
+    mx = row_max_ordered(mx);
     const float mn = fmaxf(st.m[a], mx);
     alpha[a] = (mn == st.m[a]) ? 1.f : (st.m[a] == -INFINITY ? 0.f : exp2_fast(st.m[a] - mn));
     moved |= (mn != st.m[a]);
@@ -263,7 +263,7 @@ __device__ __forceinline__ void gx_page(const GxPage<G>& r, int n_valid, const f
       pp[T] = mul_hi_f(p, r.vm[T]);
       pmax = fmaxf(pmax, pp[T]);
     }
-    const int ep = mx_exp(row_max(pmax));
+    const int ep = mx_exp(row_max_nonneg(pmax));
 #pragma unroll
     for (int T = 0; T < NT; ++T) pp[T] = __builtin_amdgcn_ldexpf(pp[T], 4 - ep);
     // tiles 4u..4u+3: slots 4(j >> 2) + 0..3 of tile T's 16-slot stretch of a
