@@ -139,7 +139,7 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
   // ---- scores: q'_c = q_c scale_c as digits, bias = sum_c q_c min_c
   const float qp0 = mul_hi_f(qs0, r.km[0]), qp1 = mul_hi_f(qs1, r.km[1]);
   const float bias = wave_sum(fmaf(qs0, lo_f(r.km[0]), qs1 * lo_f(r.km[1])));
-  const int eq = mx_exp(wave_max(fmaxf(fabsf(qp0), fabsf(qp1))));
+  const int eq = mx_exp(wave_max_nonneg(fmaxf(fabsf(qp0), fabsf(qp1))));
   {
     float d0[4], d1[4];
     mx_digits(qp0, eq, d0);
@@ -172,7 +172,7 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
     if (n_valid < G && t0 + 64 * i >= n_valid) z[i] = -INFINITY;  // a short page
     mx = fmaxf(mx, z[i]);
   }
-  mx = wave_max(mx);
+  mx = wave_max_ordered(mx);
   if (mx == -INFINITY) return;  // a page without members
   rescale_q(st, fmaxf(st.m, mx));
   // ---- values: p'_t = p_t scale_t as digits
@@ -186,7 +186,7 @@ __device__ __forceinline__ void mx_page(const MxPage<G>& r, int n_valid, float q
     pp[i] = mul_hi_f(p, r.vm[i]);
     pmax = fmaxf(pmax, pp[i]);
   }
-  const int ep = mx_exp(wave_max(pmax));
+  const int ep = mx_exp(wave_max_nonneg(pmax));
   {
     // slot t0 + 64i sits in block i/2 at mx_k(t0) + 64 (i & 1); at G = 256 in
     // block t0 / 32 at mx_k(t0 % 32) + 32i

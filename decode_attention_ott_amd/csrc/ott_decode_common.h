@@ -94,6 +94,22 @@ __device__ __forceinline__ float wave_max(float x) {
   p = swap32(x);
   return fmaxf(p.x, p.y);
 }
+// wave maxima through the same unsigned order (see row_max_u32)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_max_u32(v);
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(uint32_t(r[0]), uint32_t(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  return __uint_as_float(wave_max_u32(__float_as_uint(x) & 0x7fffffffu));
+}
+__device__ __forceinline__ float wave_max_ordered(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t u = wave_max_u32(b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u));
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
 __device__ __forceinline__ float pair_sum(float x) { return x + dpp<kQuadSwap1>(x); }
 
 // Orders this wave's LDS writes before its later LDS reads. A wave's LDS
