@@ -31,19 +31,12 @@ constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
-// every lane of a 16-lane row receives the row's sum / max
+// every lane of a 16-lane row receives the row's sum
 __device__ __forceinline__ float row_sum(float x) {
   x += dpp<kQuadSwap1>(x);
   x += dpp<kQuadSwap2>(x);
   x += dpp<kHalfMirror>(x);
   x += dpp<kRowMirror>(x);
-  return x;
-}
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp<kQuadSwap1>(x));
-  x = fmaxf(x, dpp<kQuadSwap2>(x));
-  x = fmaxf(x, dpp<kHalfMirror>(x));
-  x = fmaxf(x, dpp<kRowMirror>(x));
   return x;
 }
 // Row maxima compared as unsigned integers: a float's bits with the sign bit
@@ -86,13 +79,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   x = p.x + p.y;
   p = swap32(x);
   return p.x + p.y;
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = row_max(x);
-  f32x2 p = swap16(x);
-  x = fmaxf(p.x, p.y);
-  p = swap32(x);
-  return fmaxf(p.x, p.y);
 }
 // wave maxima through the same unsigned order (see row_max_u32)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
