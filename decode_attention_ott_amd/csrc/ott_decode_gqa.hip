@@ -121,11 +121,10 @@ __device__ __forceinline__ i32x8 gx_a(const uint8_t* blk, int lane) {
 
 // Scale register of lane l: row l & 15 = digit (l & 3) of head (l & 15) >> 2,
 // whose exponent e lives in lane group (l & 15) >> 2; times 2 for code/2.
+// One backward permute fetches it from lane 16 ((l & 15) >> 2) (byte address
+// four times the lane).
 __device__ __forceinline__ int gx_scale(int e, int lane) {
-  const int e0 = __builtin_amdgcn_readlane(e, 0), e1 = __builtin_amdgcn_readlane(e, 16);
-  const int e2 = __builtin_amdgcn_readlane(e, 32), e3 = __builtin_amdgcn_readlane(e, 48);
-  const int h = (lane & 15) >> 2;
-  const int eh = h == 0 ? e0 : h == 1 ? e1 : h == 2 ? e2 : e3;
+  const int eh = __builtin_amdgcn_ds_bpermute((lane & 12) << 4, e);
   return 124 + eh - 5 * (lane & 3);
 }
 
