@@ -9,8 +9,8 @@
 // every wave keeps a running max m, a running sum l and an accumulator, and
 // partial states merge as (m, l, acc) -> (M, sum l e^(m-M), sum acc e^(m-M)).
 //
-// A split is a byte-balanced slice of one (sequence, KV head)'s cache: a range
-// of pages and a range of fp16 tokens (pool first, then the window). With one
+// A split is an even share of one (sequence, KV head)'s pages and an even
+// share of its fp16 tokens (pool first, then the window). With one
 // split the work-group writes the output; otherwise every split writes its
 // partial state and takes a ticket, and the head's last split to arrive merges
 // all of them in the same launch (no second kernel, no launch gap).
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
     if (threadIdx.x >= D && threadIdx.x < D + 32) piece = step_row_piece(step, bh, threadIdx.x - D);
   const int pc = min(a.P, a.G * nb);
   const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
-  const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
+  const Split sp = split_of(nb, pc + r_cnt + n_new, s, S);
   const int p1 = sp.p1, t1 = sp.t1;
   const int buf = nb & 1;
   const Fp16Src base_src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.acc[k] = 0.f;
   // fp16 chunks (memory-heavy) are spread between pages (compute-heavy),
-  // staggered by wave, so the work-group always mixes the two
-  int chunk = sp.t0 + wave * kF16Chunk;
+  // staggered by wave, so the work-group always mixes the two. A split of
+  // several holds a chunk or so: it goes to a wave with fewer pages.
+  int chunk = S > 1 ? first_chunk(sp, wave) : sp.t0 + wave * kF16Chunk;
   auto next_chunk = [&]() {
     Fp16State fs;
     fs.m = -INFINITY;
@@ -327,6 +328,13 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
     st.acc[4] += (L.fin[0][ca + 64] + L.fin[1][ca + 64]) + (L.fin[2][ca + 64] + L.fin[3][ca + 64]);
     wave_lds_sync();
   };
+  // With one split every CU holds several heads' work-groups, dispatched one
+  // after another. A short pause after the query loads and before the page
+  // loads lets the work-groups dispatched last read their counters and query
+  // before the page loads of the first ones fill the memory queues (without
+  // it their counters arrived ~1.8 us late and they finished last; at 32
+  // sequences x 32 heads of 3-4K tokens, 51.4 against 53.2 us per decode).
+  if (S == 1) __builtin_amdgcn_s_sleep(8);
   int n = 0;
   for (int u = sp.p0 + wave; u < p1; u += kWaves, ++n) {
     prio_by_work_left((p1 - u + kWaves - 1) / kWaves);

@@ -16,7 +16,6 @@ namespace dec {
 using namespace dev;
 
 constexpr int kWaves = 4;           // waves (work items) per work-group
-constexpr int kFp16TokenBytes = 4 * D;  // K + V bytes of one fp16 token
 
 // ---------------------------------------------------------------------------
 // cross-lane helpers (DPP inside 16-lane rows, permlane swaps across rows)
@@ -330,21 +329,20 @@ __device__ __forceinline__ void fp16_chunk(const Src& src, int base, int cnt, co
   fp16_attend(r, cnt, q8, qscale, st, lane);
 }
 
-// Byte-balanced split of one (sequence, KV head)'s cache: split s of S takes
-// the pages [p0, p1) and the fp16 tokens [t0, t1) whose bytes fall in the
-// s-th S-th of the head's bytes (pages first, then fp16 tokens).
+// Split s of S of one (sequence, KV head)'s cache: the pages [p0, p1) and the
+// fp16 tokens [t0, t1) of an even share of each, so that every split holds
+// about the same page bytes and a chunk or so of fp16 tokens (their chunk
+// loads, one dependent wait each, are not left to one split).
 struct Split {
   int p0, p1, t0, t1;
 };
-__device__ __forceinline__ Split split_of(int nb, int n16, int64_t PB, int s, int S) {
-  const int64_t W = nb * PB + int64_t(n16) * kFp16TokenBytes;
-  const int64_t lo = int64_t(s) * W / S, hi = int64_t(s + 1) * W / S;
-  auto first_page = [&](int64_t x) { return int(min<int64_t>(nb, (x + PB - 1) / PB)); };
-  auto first_tok = [&](int64_t x) {
-    const int64_t r = x - nb * PB;
-    return r <= 0 ? 0 : int(min<int64_t>(n16, (r + kFp16TokenBytes - 1) / kFp16TokenBytes));
-  };
-  return Split{first_page(lo), first_page(hi), first_tok(lo), first_tok(hi)};
+__device__ __forceinline__ Split split_of(int nb, int n16, int s, int S) {
+  return Split{s * nb / S, (s + 1) * nb / S, s * n16 / S, (s + 1) * n16 / S};
+}
+// First fp16 chunk of wave w in a split: chunks are dealt from the last wave
+// down, since the last waves hold the fewest of the split's pages.
+__device__ __forceinline__ int first_chunk(const Split& sp, int wave) {
+  return sp.t0 + (kWaves - 1 - wave) * kF16Chunk;
 }
 
 // Partial state of split s for (sequence b, query head qh): {m, l, acc[D]}.

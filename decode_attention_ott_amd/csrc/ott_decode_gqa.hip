@@ -318,6 +318,10 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   __shared__ GxLds<G, NA> lds_all[kWaves];
   __shared__ float mg_m[kWaves][QB], mg_l[kWaves][QB];
   __shared__ uint32_t mg_last;
+  // The prologue (counters, query rows, fp16 chunks) is a chain of dependent
+  // loads: at the top priority, a work-group that starts beside others
+  // already in their page loops is not held back by them.
+  __builtin_amdgcn_s_setprio(3);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, g = lane >> 4;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
   const int pc = min(a.P, a.G * nb);
   const int n_new = kStep ? 1 : 0;  // a fused step's new token, after the window
-  const Split sp = split_of(nb, pc + r_cnt + n_new, a.page_bytes, s, S);
+  const Split sp = split_of(nb, pc + r_cnt + n_new, s, S);
   const int buf = nb & 1;
   const Fp16Src base_src{pool_k(a, buf, bh), pool_v(a, buf, bh), ring_k(a, bh), ring_v(a, bh), pc,
                          head, a.C};
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
 #pragma unroll
         for (int e = 0; e < 8; ++e) fs[i].acc[e] = 0.f;
       }
-      for (int ch = sp.t0 + wave * kF16Chunk; ch < sp.t1; ch += kWaves * kF16Chunk) {
+      for (int ch = first_chunk(sp, wave); ch < sp.t1; ch += kWaves * kF16Chunk) {
         const int cnt = min(kF16Chunk, sp.t1 - ch);
         Fp16Rows rows;
         fp16_load(src, ch, cnt, rows, lane);
