@@ -258,6 +258,11 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   __shared__ WaveLds<G> lds_all[kWaves];
   __shared__ float mg_m[kWaves], mg_l[kWaves];
   __shared__ uint32_t mg_last;
+  // The prologue (head order, counters, query) is a chain of dependent loads:
+  // at the top priority it is not held back by the waves of work-groups
+  // already in their page loops (each page then sets the priority by the
+  // work left).
+  __builtin_amdgcn_s_setprio(3);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   WaveLds<G>& L = lds_all[wave];
