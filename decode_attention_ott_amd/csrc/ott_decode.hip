@@ -269,6 +269,13 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
   const int s = blockIdx.x % S;
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);  // = b * H + h
   const int b = bh / a.Hkv;
+  // the query row is read before the counters, so the two reads wait together
+  const float qscale = a.sm_scale * kLog2e;
+  const __half* qrow = q + size_t(bh) * D;
+  const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
+  // the lane's two channels: those of logical k = 2 lane, 2 lane + 1
+  const int c0 = mx_item(2 * lane);
+  const float qs0 = __half2float(qrow[c0]) * qscale, qs1 = __half2float(qrow[c0 + 2]) * qscale;
 
   const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
@@ -290,15 +297,8 @@ __global__ __launch_bounds__(256, G <= 128 ? 4 : 3) void decode_kernel(Arena a, 
     else
       return base_src;
   }();
-  const float qscale = a.sm_scale * kLog2e;
   const uint8_t* pages = page_ptr(a, bh, 0);
   const int64_t PB = a.page_bytes;
-
-  const __half* qrow = q + size_t(bh) * D;
-  const uint4 q8 = reinterpret_cast<const uint4*>(qrow)[lane & 15];
-  // the lane's two channels: those of logical k = 2 lane, 2 lane + 1
-  const int c0 = mx_item(2 * lane);
-  const float qs0 = __half2float(qrow[c0]) * qscale, qs1 = __half2float(qrow[c0 + 2]) * qscale;
   WaveState st;
   st.m = -INFINITY;
   st.l = 0.f;

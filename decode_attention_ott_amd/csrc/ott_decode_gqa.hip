@@ -330,6 +330,17 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
   const int s = blockIdx.x % S;
   const int bh = order.n ? int(order.bh[blockIdx.x]) : int(blockIdx.x / S);
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  // Query row h of the KV head's group, the lane's 16 bytes (channels
+  // 8(lane & 15)..+7); zero past the group's last head.
+  const __half* qkv = q + (size_t(b) * a.Hq + size_t(hk) * NQ) * D;
+  auto q_row = [&](int h) {
+    return h < NQ ? reinterpret_cast<const uint4*>(qkv + size_t(h) * D)[j] : make_uint4(0u, 0u, 0u, 0u);
+  };
+  // The page loop's query values (head 4x + g, channels 8j..8j+7) of the first
+  // pass are read before the counters, so the two reads wait together.
+  uint4 mine_first[NA];
+#pragma unroll
+  for (int x = 0; x < NA; ++x) mine_first[x] = q_row(4 * x + g);
 
   const HeadCtr hc = head_counters<kStep>(a, step, b, bh);
   const int r_cnt = hc.r_cnt, head = hc.head, nb = hc.nb;
@@ -351,7 +362,6 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
 
   for (int q0 = 0; q0 < NQ; q0 += QB) {
     const int qh0 = hk * NQ + q0;
-    const __half* qbase = q + (size_t(b) * a.Hq + qh0) * D;
     GxState<NA> st;
 #pragma unroll
     for (int x = 0; x < NA; ++x) {
@@ -365,15 +375,23 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
     // fp16 tokens: each chunk is loaded once per group of 4 heads; the heads'
     // states then become the (still empty) page states, the accumulator in
     // digit row 0
+    float qs[NA][8];  // the lane's query values for the q' step: head 4x + g, channels 8j..8j+7
 #pragma unroll
     for (int x = 0; x < NA; ++x) {
-      uint4 q8[4];
+      {
+        const uint4 mine = q0 == 0 ? mine_first[x] : q_row(q0 + 4 * x + g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = dw(mine, i >> 1);
+          qs[x][i] = ((i & 1) ? hi_f(w) : lo_f(w)) * qscale;
+        }
+      }
+      uint4 q8[4];  // the group's four rows, for the fp16 tokens
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q8[i] = q_row(q0 + 4 * x + i);
       Fp16State fs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool live = q0 + 4 * x + i < NQ;
-        q8[i] = live ? reinterpret_cast<const uint4*>(qbase + size_t(4 * x + i) * D)[lane & 15]
-                     : make_uint4(0u, 0u, 0u, 0u);
         fs[i].m = -INFINITY;
         fs[i].l = 0.f;
 #pragma unroll
@@ -413,22 +431,6 @@ __global__ __launch_bounds__(256, NA == 1 ? (G <= 128 ? 3 : 2) : 1) void decode_
       }
     }
 
-    // the lane's query values for the q' step: head 4x + g, channels 8j..8j+7
-    float qs[NA][8];
-#pragma unroll
-    for (int x = 0; x < NA; ++x) {
-      if (q0 + 4 * x + g < NQ) {
-        const uint4 q8 = *reinterpret_cast<const uint4*>(qbase + size_t(4 * x + g) * D + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w = dw(q8, i >> 1);
-          qs[x][i] = ((i & 1) ? hi_f(w) : lo_f(w)) * qscale;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qs[x][i] = 0.f;
-      }
-    }
 
     // pages, each wave every 4th
     for (int u = sp.p0 + wave; u < sp.p1; u += kWaves) {
