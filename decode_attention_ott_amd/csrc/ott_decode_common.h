@@ -329,15 +329,18 @@ __device__ __forceinline__ void fp16_chunk(const Src& src, int base, int cnt, co
   fp16_attend(r, cnt, q8, qscale, st, lane);
 }
 
-// Split s of S of one (sequence, KV head)'s cache: the pages [p0, p1) and the
-// fp16 tokens [t0, t1) of an even share of each, so that every split holds
-// about the same page bytes and a chunk or so of fp16 tokens (their chunk
-// loads, one dependent wait each, are not left to one split).
+// Split s of S of one (sequence, KV head)'s cache: an even share of the pages
+// [p0, p1) and an even share of the fp16 tokens [t0, t1) in whole chunks, so
+// that every split holds about the same page bytes and at most a chunk or so
+// of fp16 tokens (a chunk's load is one dependent wait whatever it holds, so
+// neither one split with all of them nor every split with a sliver of one).
 struct Split {
   int p0, p1, t0, t1;
 };
 __device__ __forceinline__ Split split_of(int nb, int n16, int s, int S) {
-  return Split{s * nb / S, (s + 1) * nb / S, s * n16 / S, (s + 1) * n16 / S};
+  const int nc = (n16 + kF16Chunk - 1) / kF16Chunk;
+  return Split{s * nb / S, (s + 1) * nb / S, min(n16, kF16Chunk * (s * nc / S)),
+               min(n16, kF16Chunk * ((s + 1) * nc / S))};
 }
 // First fp16 chunk of wave w in a split: chunks are dealt from the last wave
 // down, since the last waves hold the fewest of the split's pages.
