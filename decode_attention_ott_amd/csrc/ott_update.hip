@@ -7,13 +7,16 @@
 //   append_kernel    fp16 window update ([Blog] 3.3, residual window)
 //   quantize_kernel  quantization stage: Key norms, pool competition, 2-bit
 //                    pages ([Blog] 3.1, 3.2, flowchart; [Abs] Fig. 2 bottom)
-//   prefill_select_kernel, prefill_pack_kernel  a whole prompt through the same
-//                    steps: the pool walk per head in order, then every page at once
+//   prefill_top_kernel, prefill_select_kernel, prefill_pack_kernel  a whole
+//                    prompt through the same steps: each segment's smallest P,
+//                    the pool walk per segment, then every page at once
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "ott_device.h"
 
@@ -595,12 +598,23 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
 // prefill: a prompt of L_b tokens per sequence into an empty cache, with the
 // same result as appending it and running every due quantize step in order.
 // A window is full at R+G tokens and a step removes G, so the prompt makes
-// nq = floor((L - R) / G) pages (0 when L < R + G). Two kernels:
-//   prefill_select_kernel  one work-group per (sequence, KV head) walks the
-//       groups in position order on keys alone (the pool's keys and positions
-//       stay in LDS from step to step): each step's members go to the page's
-//       member list; then the final pool and the one before it (the two pool
-//       buffers single steps would leave) and the window.
+// nq = floor((L - R) / G) pages (0 when L < R + G).
+// The pool after step n holds the P smallest (key, position) pairs of all the
+// tokens of groups 0..n: a step keeps the P smallest of the pool and the group,
+// and the P smallest of a union are among the P smallest of each of its parts.
+// So the groups are cut into segments of `seg` groups, and a segment's walk
+// can start from the merge of the earlier segments' own P smallest. Kernels,
+// after prefill_norms_kernel:
+//   prefill_top_kernel     one work-group per (segment, sequence, KV head):
+//       the segment's P smallest pairs, ascending (a radix select on the key
+//       bits, ties in position order), into the segment's page slots.
+//   prefill_select_kernel  one work-group per (segment, sequence, KV head):
+//       the start pool from the earlier segments' tops, then the walk over the
+//       segment's groups in position order on keys alone (the pool's keys and
+//       positions stay in LDS from step to step): each step's members go to
+//       the page's member list; the last segment then writes the final pool
+//       and the one before it (the two pool buffers single steps would leave),
+//       the window and the counters.
 //   prefill_pack_kernel    one work-group per page: the page bytes from its
 //       members' rows, read from the prompt by position.
 // ---------------------------------------------------------------------------
@@ -625,15 +639,215 @@ __global__ __launch_bounds__(256) void prefill_norms_kernel(Arena a, const __hal
   for (int j = threadIdx.x; j < a.G; j += blockDim.x) out[j] = sq_norm_fp64(kb + size_t(j) * D);
 }
 
-__global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
+// Unsigned bits of a retention key that order as the key does: negative keys
+// inverted, non-negative ones with the top bit set. Zeros come with one sign
+// under every rule (a norm is +0, its negation -0, a random fraction +0), so
+// equal keys have equal bits.
+__device__ __forceinline__ uint64_t key_bits(double x) {
+  const uint64_t u = uint64_t(__double_as_longlong(x));
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+__device__ __forceinline__ double key_of_bits(uint64_t u) {
+  return __longlong_as_double((long long)((u >> 63) ? (u & ~(1ull << 63)) : ~u));
+}
+__device__ __forceinline__ uint64_t shr64(uint64_t u, int n) { return n >= 64 ? 0 : u >> n; }
+
+// A segment's smallest (key, position) pairs, ascending, sit in the free bytes
+// of its own page slots (bytes [8 G, page_bytes) of each, rounded down to 8,
+// after the slot's norms): P keys, then P positions. The pack overwrites them.
+__device__ __forceinline__ uint8_t* seg_top_at(const Arena& a, int bh, int g0, size_t off) {
+  const size_t f = (size_t(a.page_bytes) - 8 * size_t(a.G)) & ~size_t(7);
+  return page_ptr(a, bh, g0 + int(off / f)) + 8 * size_t(a.G) + off % f;
+}
+__device__ __forceinline__ double* seg_top_key(const Arena& a, int bh, int g0, int i) {
+  return reinterpret_cast<double*>(seg_top_at(a, bh, g0, 8 * size_t(i)));
+}
+__device__ __forceinline__ int32_t* seg_top_pos(const Arena& a, int bh, int g0, int i) {
+  return reinterpret_cast<int32_t*>(seg_top_at(a, bh, g0, 8 * size_t(a.P) + 4 * size_t(i)));
+}
+
+constexpr int kTopPerThread = 8;  // a segment holds at most 8 * 1024 tokens
+constexpr int kMaxPool = 512;
+
+// The min(P, seg G) smallest (key, position) pairs of segment blockIdx.x's
+// tokens, ascending. Radix select from the top bit that differs between the
+// smallest and largest key, 8 bits a pass: a histogram of the next digit among
+// the tokens still on the boundary picks the digit where the count reaches P.
+// The pairs below the final boundary are all taken; on it, the first ones in
+// position order. Then ranked by (key, position). The last segment of a
+// sequence has no successor to read its pairs and is skipped.
+__global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, PrefillLens lens,
+                                                                    int seg) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t red[2][kQuantThreads / 64];
+  __shared__ int pick[3];  // digit, pairs below it, pairs on it
+  __shared__ int wcnt[kQuantThreads / 64];
+  __shared__ int n_sel;
+  __shared__ double sel_k[kMaxPool];
+  __shared__ int32_t sel_p[kMaxPool];
+  __shared__ int sel_r[kMaxPool];
+  const int sg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bh = b * a.Hkv + h;
+  const int nq = prefill_pages(a, lens.len[b]);
+  const int g0 = sg * seg;
+  if (g0 + seg >= nq) return;
+  const int G = a.G, n = seg * G, take = min(a.P, n);
+  if (take == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int kWavesT = kQuantThreads / 64;
+
+  uint64_t u[kTopPerThread];
+  uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+  for (int k = 0; k < kTopPerThread; ++k) {
+    const int j = tid + k * kQuantThreads;
+    u[k] = 0;
+    if (j < n) {
+      const double x = retention_key(prefill_norms(a, bh, g0 + j / G)[j % G], g0 * G + j,
+                                     a.retention);
+      u[k] = key_bits(x);
+      mn = min(mn, u[k]);
+      mx = max(mx, u[k]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    red[0][wv] = mn;
+    red[1][wv] = mx;
+  }
+  if (tid == 0) n_sel = 0;
+  __syncthreads();
+  mn = red[0][0];
+  mx = red[1][0];
+  for (int w = 1; w < kWavesT; ++w) {
+    mn = min(mn, red[0][w]);
+    mx = max(mx, red[1][w]);
+  }
+  // boundary: tokens whose bits above `lo` equal `pre` (`bin` of them);
+  // `need` of them are still to be taken
+  int need = take, bin = n, lo = 0;
+  uint64_t pre = mn;
+  if (mn != mx) {
+    lo = 64 - __clzll((long long)(mn ^ mx));
+    pre = shr64(mn, lo);
+    while (lo > 0) {
+      const int nlo = max(lo - 8, 0);
+      const uint32_t mask = (1u << (lo - nlo)) - 1u;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kTopPerThread; ++k)
+        if (tid + k * kQuantThreads < n && shr64(u[k], lo) == pre)
+          atomicAdd(&hist[uint32_t(u[k] >> nlo) & mask], 1u);
+      __syncthreads();
+      if (wv == 0) {
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = hist[4 * lane + i];
+          sum += c[i];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        uint32_t below = incl - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (below < uint32_t(need) && uint32_t(need) <= below + c[i]) {
+            pick[0] = 4 * lane + i;
+            pick[1] = int(below);
+            pick[2] = int(c[i]);
+          }
+          below += c[i];
+        }
+      }
+      __syncthreads();
+      pre = (pre << (lo - nlo)) | uint64_t(pick[0]);
+      need -= pick[1];
+      bin = pick[2];
+      lo = nlo;
+      if (bin == need) break;  // the whole boundary is taken
+    }
+  }
+  // take the pairs below the boundary, and the first `need` on it
+  const bool split = bin > need;  // only with lo == 0: equal keys, by position
+  int tie_base = 0;
+#pragma unroll
+  for (int k = 0; k < kTopPerThread; ++k) {
+    const int j = tid + k * kQuantThreads;
+    const bool valid = j < n;
+    const uint64_t hb = shr64(u[k], lo);
+    const bool tie = valid && hb == pre;
+    bool taken = valid && hb < pre;
+    if (split) {
+      if (k * kQuantThreads >= n) break;  // uniform
+      const uint64_t ball = __ballot(tie);
+      const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(ball >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(uint32_t(ball), 0));
+      if (lane == 0) wcnt[wv] = __popcll(ball);
+      __syncthreads();
+      int before = 0, total = 0;
+      for (int w = 0; w < kWavesT; ++w) {
+        total += wcnt[w];
+        if (w < wv) before += wcnt[w];
+      }
+      __syncthreads();
+      taken = taken || (tie && tie_base + before + below < need);
+      tie_base += total;
+    } else {
+      taken = taken || tie;
+    }
+    if (taken) {  // exactly `take` of them
+      const int slot = atomicAdd(&n_sel, 1);
+      if (slot < kMaxPool) {
+        sel_k[slot] = key_of_bits(u[k]);
+        sel_p[slot] = g0 * G + j;
+      }
+    }
+  }
+  for (int i = tid; i < take; i += blockDim.x) sel_r[i] = 0;
+  __syncthreads();
+  // ranks under (key, position), `parts` threads per pair
+  const int parts = max(1, int(blockDim.x) / take);
+  const int span = (take + parts - 1) / parts;
+  for (int x = tid; x < take * parts; x += blockDim.x) {
+    const int i = x % take, j0 = (x / take) * span, j1 = min(take, j0 + span);
+    const double ki = sel_k[i];
+    const int pi = sel_p[i];
+    int r = 0;
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) {
+      const double kj = sel_k[j];
+      r += int(kj < ki) | (int(kj == ki) & int(sel_p[j] < pi));
+    }
+    if (r) atomicAdd(&sel_r[i], r);
+  }
+  __syncthreads();
+  for (int i = tid; i < take; i += blockDim.x) {
+    *seg_top_key(a, bh, g0, sel_r[i]) = sel_k[i];
+    *seg_top_pos(a, bh, g0, sel_r[i]) = sel_p[i];
+  }
+}
+
+// Two work-groups per CU (8 waves per SIMD): the walk's steps are short phases
+// between barriers, which a second work-group fills.
+__global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void prefill_select_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
-    PrefillLens lens) {
+    PrefillLens lens, int seg) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int sg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.Hkv + h;
   const int L = lens.len[b];
   if (L == 0) {  // an empty sequence still gets its counters (the arena is not zeroed)
-    if (threadIdx.x == 0) {
+    if (sg == 0 && threadIdx.x == 0) {
       int32_t* ctr = counters(a, bh);
       ctr[0] = ctr[1] = ctr[2] = ctr[3] = 0;
       reset_ticket(a, bh);
@@ -643,22 +857,61 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
   const int G = a.G, P = a.P, C = a.C;
   const int tid = threadIdx.x;
   const int nq = prefill_pages(a, L);
+  const int g0 = sg * seg, g1 = min(nq, g0 + seg);
+  if (sg > 0 && g0 >= nq) return;  // segment 0 runs even without pages: it writes the window
   const __half* kb = k + size_t(bh) * max_len * D;
   const __half* vb = v + size_t(bh) * max_len * D;
-  QuantLds s = quant_lds(lds_raw, P + G, G);
+  QuantLds s = quant_lds(lds_raw, P + G, G, 0);
   // two pools of keys and positions after the QuantLds region
   double* pkey[2];
   int32_t* ppos[2];
   {
-    uint8_t* base = lds_raw + ((quant_lds_bytes(G, P) + 15) & ~size_t(15));
+    uint8_t* base = lds_raw + ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15));
     pkey[0] = reinterpret_cast<double*>(base);
     pkey[1] = pkey[0] + P;
     ppos[0] = reinterpret_cast<int32_t*>(pkey[1] + P);
     ppos[1] = ppos[0] + P;
   }
+  // the pool before step g0: the earlier segments' smallest pairs merged in
+  // order, each merge keeping the P smallest of two ascending lists (a pair's
+  // merged rank is its index plus the pairs of the other list below it); the
+  // merges alternate buffers and end in buffer g0 & 1, which step g0 reads
+  {
+    int x = (g0 + sg) & 1, pc = 0;
+    const int cb = min(P, seg * G);
+    for (int i = 0; i < sg; ++i) {
+      for (int t = tid; t < cb; t += blockDim.x) {
+        s.n2[t] = *seg_top_key(a, bh, i * seg, t);
+        s.pos[t] = *seg_top_pos(a, bh, i * seg, t);
+      }
+      __syncthreads();
+      const int npc = min(P, pc + cb);
+      for (int t = tid; t < pc + cb; t += blockDim.x) {
+        const bool in_pool = t < pc;
+        const int own = in_pool ? t : t - pc;
+        const double kk = in_pool ? pkey[x][t] : s.n2[own];
+        const int pp = in_pool ? ppos[x][t] : s.pos[own];
+        const double* ok = in_pool ? s.n2 : pkey[x];
+        const int32_t* op = in_pool ? s.pos : ppos[x];
+        int lo = 0, hi = in_pool ? cb : pc;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (ok[mid] < kk || (ok[mid] == kk && op[mid] < pp)) lo = mid + 1; else hi = mid;
+        }
+        const int r = own + lo;
+        if (r < npc) {
+          pkey[x ^ 1][r] = kk;
+          ppos[x ^ 1][r] = pp;
+        }
+      }
+      __syncthreads();
+      x ^= 1;
+      pc = npc;
+    }
+  }
   int32_t* page_pos_all = reinterpret_cast<int32_t*>(a.base + a.off_page_pos);
   int32_t* page_nv_all = reinterpret_cast<int32_t*>(a.base + a.off_page_nvalid);
-  for (int n = 0; n < nq; ++n) {
+  for (int n = g0; n < g1; ++n) {
     const int pc = min(P, G * n), NC = pc + G, npc = min(P, NC), n_valid = NC - npc;
     const int cur = n & 1;
     select_step(a, n, pkey[cur], ppos[cur], kb + size_t(n) * G * D, 0, G, s,
@@ -675,6 +928,7 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
     }
     __syncthreads();
   }
+  if (g1 < nq) return;  // a later segment finishes the sequence
   // pools: after nq steps in buffer nq & 1, after nq - 1 steps in the other one
   for (int back = 0; back < 2 && back < nq; ++back) {
     const int steps = nq - back, buf = steps & 1;
@@ -716,31 +970,159 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_select_kernel(
   }
 }
 
-__global__ __launch_bounds__(kQuantThreads) void prefill_pack_kernel(
+constexpr int kPackThreads = 512;
+
+// LDS of a prefill pack work-group: the members' rows [G][D], then the code
+// thresholds (per channel or per member) and the partial Key minima and maxima.
+__host__ __device__ inline size_t pack_lds_bytes(int G) {
+  return size_t(G) * D * sizeof(__half) + 256 * sizeof(CodeThr) + 2 * kPackThreads * sizeof(float);
+}
+
+// Half of page n's bytes, from its members' rows read from the prompt by
+// position: blockIdx.x = 2 n + half, half 0 the Key (min, scale) per channel
+// and the Key codes, half 1 the Value (min, scale) per member and the Value
+// codes. The members' rows are loaded into LDS once, all in one round trip;
+// the arithmetic is that of a single quantize step.
+__global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
     PrefillLens lens) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = blockIdx.x >> 1, half = blockIdx.x & 1, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.Hkv + h;
-  const int L = lens.len[b];
-  if (n >= prefill_pages(a, L)) return;
-  const int G = a.G, P = a.P;
+  if (n >= prefill_pages(a, lens.len[b])) return;
+  const int G = a.G, P = a.P, tid = threadIdx.x;
   const int pc = min(P, G * n);
   const int n_valid = pc + G - min(P, pc + G);
-  const __half* kb = k + size_t(bh) * max_len * D;
-  const __half* vb = v + size_t(bh) * max_len * D;
-  QuantLds s = quant_lds(lds_raw, P + G, G);
+  __half* rows = reinterpret_cast<__half*>(lds_raw);  // member t's row at t * D
+  CodeThr* thr = reinterpret_cast<CodeThr*>(lds_raw + size_t(G) * D * sizeof(__half));
+  float* plo = reinterpret_cast<float*>(thr + 256);
+  float* phi = plo + kPackThreads;
+  const __half* src = (half ? v : k) + size_t(bh) * max_len * D;
   const int32_t* pp = reinterpret_cast<const int32_t*>(a.base + a.off_page_pos) +
                       (size_t(bh) * a.nb_max + n) * G;
-  for (int t = threadIdx.x; t < n_valid; t += blockDim.x) {
-    s.src[t] = pp[t];  // a position in the prompt
-    s.mem[t] = t;
+  uint8_t* pg = page_ptr(a, bh, n);
+  {
+    // thread tid moves 16-byte piece tid % 16 of members tid / 16 + 32 r: the
+    // positions first, then every row load at once (past the members, row 0
+    // of the prompt, which a page's existence guarantees, is read and dropped)
+    constexpr int kRounds = 256 * (D / 8) / kPackThreads;
+    const int c8 = tid % (D / 8), t0 = tid / (D / 8);
+    int pos[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int t = t0 + r * (kPackThreads / (D / 8));
+      pos[r] = t < n_valid ? pp[t] : 0;
+    }
+    uint4 x[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+      x[r] = reinterpret_cast<const uint4*>(src + size_t(pos[r]) * D)[c8];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int t = t0 + r * (kPackThreads / (D / 8));
+      if (t < n_valid) reinterpret_cast<uint4*>(rows)[t * (D / 8) + c8] = x[r];
+    }
   }
   __syncthreads();
-  auto krow = [&](int pos) -> const __half* { return kb + size_t(pos) * D; };
-  auto vrow = [&](int pos) -> const __half* { return vb + size_t(pos) * D; };
-  pack_page(a, page_ptr(a, bh, n), s, n_valid,
-            StagedRows<decltype(krow), decltype(vrow)>{krow, vrow});
+  if (half == 0) {
+    // Key (min, scale) per channel: 4 partial scans, then one thread per channel
+    constexpr int kParts = kPackThreads / D;
+    {
+      const int c = tid % D, part = tid / D;
+      float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 4
+      for (int t = part; t < n_valid; t += kParts) {
+        const float x = __half2float(rows[t * D + c]);
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+      }
+      plo[tid] = lo;
+      phi[tid] = hi;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float lo = plo[tid], hi = phi[tid];
+#pragma unroll
+      for (int p2 = 1; p2 < kParts; ++p2) {
+        lo = fminf(lo, plo[p2 * D + tid]);
+        hi = fmaxf(hi, phi[p2 * D + tid]);
+      }
+      if (n_valid == 0) lo = hi = 0.f;
+      const uint32_t lo_b = meta_bits(lo);
+      const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
+      thr[(tid % 16) * (D / 16) + tid / 16] =
+          code_thresholds(__half2float(__ushort_as_half(uint16_t(lo_b))),
+                          __half2float(__ushort_as_half(uint16_t(sc_b))));
+      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = lo_b | (sc_b << 16);
+    }
+    __syncthreads();
+    // codes, token-major: dword (t, j) = channels 16 j .. 16 j + 15 of member
+    // t (zero past the members); channel 16 j + cc's thresholds at cc * 8 + j
+    uint32_t* kc = reinterpret_cast<uint32_t*>(pg + kcode_off(G));
+    for (int w = tid; w < G * (D / 16); w += kPackThreads) {
+      const int t = w / (D / 16), j = w % (D / 16);
+      uint32_t word = 0;
+      if (t < n_valid) {
+        const uint4* row = reinterpret_cast<const uint4*>(rows + t * D + 16 * j);
+        const uint4 r0 = row[0], r1 = row[1];
+        const uint32_t hw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+          const uint16_t bits = uint16_t(cc & 1 ? hw[cc >> 1] >> 16 : hw[cc >> 1] & 0xffffu);
+          word |= qcode(__half2float(__ushort_as_half(bits)), thr[cc * (D / 16) + j]) << (2 * cc);
+        }
+      }
+      kc[w] = word;
+    }
+    return;
+  }
+  // Value (min, scale) per member: 8 lanes per member, 16 channels each
+  // (rotated per member against bank conflicts), combined by lane swaps
+  uint32_t* vmeta = reinterpret_cast<uint32_t*>(pg + vmeta_off(G));
+  for (int tb = 0; tb < G; tb += kPackThreads / 8) {
+    const int t = tb + (tid >> 3), part = tid & 7;
+    float mn = INFINITY, mx = -INFINITY;
+    if (t < n_valid) {
+      const __half* row = rows + t * D;
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (t < G && part == 0) {
+      if (t < n_valid) {
+        const uint32_t mn_b = meta_bits(mn);
+        const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+        thr[t] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
+                                 __half2float(__ushort_as_half(uint16_t(sc_b))));
+        vmeta[t] = mn_b | (sc_b << 16);
+      } else {
+        vmeta[t] = 0u;
+      }
+    }
+  }
+  __syncthreads();
+  // codes, channel-major: dword (c, j) = members 16 j .. 16 j + 15 of channel c
+  // (zero past the members)
+  uint32_t* vc = reinterpret_cast<uint32_t*>(pg + vcode_off(G));
+  const int vdw = G / 16;
+  for (int w = tid; w < D * vdw; w += kPackThreads) {
+    const int c = w % D, j = w / D;
+    uint32_t word = 0;
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) {
+      const int t = 16 * j + cc;
+      if (t < n_valid) word |= qcode(__half2float(rows[t * D + c]), thr[t]) << (2 * cc);
+    }
+    vc[c * vdw + j] = word;
+  }
 }
 
 }  // namespace
@@ -756,22 +1138,41 @@ hipError_t launch_append(const Arena& a, const void* k, const void* v, const App
 size_t quantize_lds_bytes(int G, int P) { return quant_lds_bytes(G, P); }
 
 size_t prefill_select_lds_bytes(int G, int P) {
-  return ((quant_lds_bytes(G, P) + 15) & ~size_t(15)) + size_t(P) * 2 * (sizeof(double) + 4);
+  return ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15)) + size_t(P) * 2 * (sizeof(double) + 4);
+}
+
+// Groups per prefill segment: enough segments for about two walk work-groups
+// per CU (at most 64, since a segment merges every earlier segment's pairs),
+// no more tokens than prefill_top_kernel holds, and page slots enough for the
+// segment's pairs (12 P bytes). One segment when the heads alone fill the GPU.
+int prefill_segment(const Arena& a, int max_pages, int cus) {
+  if (max_pages <= 1 || a.P == 0) return max(max_pages, 1);
+  const size_t f = (size_t(a.page_bytes) - 8 * size_t(a.G)) & ~size_t(7);
+  const int smin = int((12 * size_t(a.P) + f - 1) / f);
+  const int smax = kTopPerThread * kQuantThreads / a.G;
+  if (smin > smax) return max_pages;
+  const int64_t heads = int64_t(a.B) * a.Hkv;
+  const int64_t want =
+      std::min<int64_t>(64, std::max<int64_t>(1, (2 * int64_t(cus) + heads - 1) / heads));
+  if (want == 1) return max_pages;
+  const int seg = int((max_pages + want - 1) / want);
+  return std::min(std::max(seg, smin), smax);
 }
 
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
-                          const PrefillLens& lens, int max_pages, hipStream_t s) {
+                          const PrefillLens& lens, int max_pages, int cus, hipStream_t s) {
   const size_t lds_sel = prefill_select_lds_bytes(a.G, a.P);
-  const size_t lds = quantize_lds_bytes(a.G, a.P);
   if (lds_sel > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_select_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              int(lds_sel));
     if (e != hipSuccess) return e;
   }
-  if (lds > 65536) {
+  const size_t lds_pack = pack_lds_bytes(a.G);
+  if (lds_pack > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_pack_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int(lds_pack));
     if (e != hipSuccess) return e;
   }
   const __half* kh = static_cast<const __half*>(k);
@@ -782,12 +1183,20 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prefill_select_kernel, dim3(a.Hkv, a.B), dim3(kQuantThreads), lds_sel, s, a,
-                     kh, vh, max_len, lens);
+  const int seg = prefill_segment(a, max_pages, cus);
+  const int nseg = max_pages > 0 ? (max_pages + seg - 1) / seg : 1;
+  if (nseg > 1) {
+    hipLaunchKernelGGL(prefill_top_kernel, dim3(nseg - 1, a.Hkv, a.B), dim3(kQuantThreads), 0, s,
+                       a, lens, seg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(prefill_select_kernel, dim3(nseg, a.Hkv, a.B), dim3(kQuantThreads), lds_sel,
+                     s, a, kh, vh, max_len, lens, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_pages == 0) return e;
-  hipLaunchKernelGGL(prefill_pack_kernel, dim3(max_pages, a.Hkv, a.B), dim3(kQuantThreads), lds, s,
-                     a, kh, vh, max_len, lens);
+  hipLaunchKernelGGL(prefill_pack_kernel, dim3(2 * max_pages, a.Hkv, a.B), dim3(kPackThreads),
+                     lds_pack, s, a, kh, vh, max_len, lens);
   return hipGetLastError();
 }
 

@@ -54,12 +54,14 @@ def _state(layer):
     return st
 
 
-def _compare(w, lengths):
+def _compare(w, lengths, keys=None):
     import torch
     from decode_attention_ott_amd import OTTLayer
     lengths = np.asarray(lengths, np.int64)
     n_pos = max(int(lengths.max()), 1)
     K, V = synth.kv_all(w, n_pos)
+    if keys is not None:
+        K = keys(K)
     Kd, Vd = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
     one = OTTLayer.for_workload(w, max_seq_len=n_pos + 8)
     one.prefill(Kd, Vd, lengths)
@@ -124,3 +126,27 @@ def test_prefill_rejects_a_nonempty_cache():
         fresh = OTTLayer(1, 1, 1, 128, 128, 32, 32, max_seq_len=5)
         L.ott_prefill(fresh.handle, k.data_ptr(), k.data_ptr(), [10], 10, 0)
     assert np.array_equal(layer.counters(), before)
+
+
+def _few_norms(K):
+    """Keys of 0, +1 and -1 only, most channels 0: the squared norms are small
+    integers, so most keys tie with many others (and zero rows give a zero
+    norm, negated to -0 under the largest-norm rule)."""
+    rng = np.random.default_rng(11)
+    mask = rng.random(K.shape) < 0.04
+    return (np.sign(K.astype(np.float32)) * mask).astype(np.float16)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_prefill_matches_stepwise_with_tied_keys(rule):
+    """Equal keys are ranked by position: in the pool walk, and in each
+    segment's selection of its smallest pairs, where a tie can fall on the
+    boundary of the P smallest."""
+    _compare(small(f"prefill-ties{rule}", G=64, R=16, P=40, retention=rule, seed=70 + rule),
+             [3000, 2900, 1200, 3001], keys=_few_norms)
+
+
+def test_prefill_long_prompt_with_a_large_pool():
+    """G = 64 with P = 512: a segment's 512 smallest pairs take the spare bytes
+    of two page slots; dozens of segments, each merging all earlier ones."""
+    _compare(small("prefill-long", G=64, R=64, P=512, Hkv=1, seed=77), [4100, 3000, 64, 700])
