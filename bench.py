@@ -340,6 +340,49 @@ def sweep_batch(args, batches):
             "speedup": round(fb["decode_us"] / ott_us, 3)}), flush=True)
 
 
+def time_prefill(args, reps: int = 5) -> None:
+    """ott_prefill of the workload's prompts into an empty cache: one JSON line
+    with the median over `reps` calls (after one untimed call) of the time between
+    HIP events on the launch stream around the call (layers are made beforehand).
+    Prompt bytes: the K and V rows of every prompt token and KV head (512 bytes),
+    each read at least once."""
+    import torch
+    import synth
+    from decode_attention_ott_amd import OTTLayer
+    w = synth.WORKLOADS[args.workload]
+    lengths = synth.prefill_lengths(w)
+    print(f"[prefill] generating {w.name} prompts", file=sys.stderr, flush=True)
+    K, V = synth.kv_all(w, int(lengths.max()))
+    dev = torch.device("cuda:0")
+    Kd, Vd = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
+    del K, V
+    stream = torch.cuda.current_stream()
+    times = []
+    for rep in range(reps + 1):
+        lay = OTTLayer.for_workload(w, max_seq_len=int(lengths.max()) + 1)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lay.prefill(Kd, Vd, lengths)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append(1e3 * e0.elapsed_time(e1))
+        lay.close()
+        print(f"[prefill] call {rep} done", file=sys.stderr, flush=True)
+    us = sorted(times)[len(times) // 2]
+    tokens = int(np.sum(lengths))
+    prompt_bytes = tokens * w.num_kv_heads * 2 * w.head_dim * 2
+    print(json.dumps({
+        "prefill": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads,
+        "context": f"{w.prefill[0]}-{w.prefill[1]}", "G": w.group_size, "P": w.pool_size,
+        "prefill_us": round(us, 1), "prompt_tokens_per_s": round(tokens / (us * 1e-6), 1),
+        "prompt_gb": round(prompt_bytes / 1e9, 3),
+        "prompt_gbs": round(prompt_bytes / (us * 1e-6) / 1e9, 1),
+        "calls_us": [round(t, 1) for t in times]}), flush=True)
+
+
 def accuracy(args, batch: int = 8):
     """Attention-output error of the OTT decode against exact attention over the
     same fp16 tokens (the fp16 baseline kernel), for the plain 2-bit cache
@@ -493,6 +536,8 @@ def main():
                          "for each instead of the bench line")
     ap.add_argument("--accuracy", action="store_true",
                     help="print the OTT output error against exact attention for P = 0, 32, 128")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time ott_prefill of the workload's prompts (one JSON line)")
     ap.add_argument("--sweep-params", action="store_true",
                     help="print OTT decode-only lines for G, R and P varied one at a time")
     args = ap.parse_args()
@@ -508,6 +553,9 @@ def main():
 
     if args.accuracy:
         accuracy(args)
+        return
+    if args.prefill:
+        time_prefill(args)
         return
     if args.sweep_params:
         sweep_params(args)

@@ -334,7 +334,7 @@ ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const
   int max_pages = 0;
   for (int b = 0; b < B; ++b)
     if (h_len[b] >= R + G) max_pages = std::max(max_pages, (h_len[b] - R) / G);
-  st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens, max_pages, h->cus,
+  st = after_launch(h, ott::launch_prefill(h->dev, d_k, d_v, max_len, lens, max_pages,
                                            static_cast<hipStream_t>(stream)));
   if (st != OTT_OK) return st;
   h->counters_written = true;  // the pool walk sets every head's counters, empty ones included

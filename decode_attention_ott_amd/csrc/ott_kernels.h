@@ -80,7 +80,7 @@ struct PrefillLens {
 // k, v: fp16 [B][Hkv][max_len][D]; the cache must be empty; max_pages is the
 // largest page count of any sequence (floor((L - R) / G) for L >= R + G).
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
-                          const PrefillLens& lens, int max_pages, int cus, hipStream_t s);
+                          const PrefillLens& lens, int max_pages, hipStream_t s);
 hipError_t launch_decode(const Arena& a, const void* q, void* out, int num_splits,
                          const HeadOrder& order, const StepArgs& step, hipStream_t s);
 // The decode kernel for a group of query heads per KV head (Hq > Hkv); it

@@ -666,7 +666,7 @@ __device__ __forceinline__ int32_t* seg_top_pos(const Arena& a, int bh, int g0, 
   return reinterpret_cast<int32_t*>(seg_top_at(a, bh, g0, 8 * size_t(a.P) + 4 * size_t(i)));
 }
 
-constexpr int kTopPerThread = 8;  // a segment holds at most 8 * 1024 tokens
+constexpr int kTopPerThread = 16;  // a segment holds at most 16 * 1024 tokens
 constexpr int kMaxPool = 512;
 
 // The min(P, seg G) smallest (key, position) pairs of segment blockIdx.x's
@@ -971,68 +971,78 @@ void prefill_select_kernel(
 }
 
 constexpr int kPackThreads = 512;
+constexpr int kPackRowBytes = 32768;  // member rows a pack work-group holds in LDS
 
-// LDS of a prefill pack work-group: the members' rows [G][D], then the code
+// LDS of a prefill pack work-group: the rows of its slice, then the code
 // thresholds (per channel or per member) and the partial Key minima and maxima.
-__host__ __device__ inline size_t pack_lds_bytes(int G) {
-  return size_t(G) * D * sizeof(__half) + 256 * sizeof(CodeThr) + 2 * kPackThreads * sizeof(float);
+__host__ __device__ inline size_t pack_lds_bytes() {
+  return kPackRowBytes + 256 * sizeof(CodeThr) + 2 * kPackThreads * sizeof(float);
 }
 
-// Half of page n's bytes, from its members' rows read from the prompt by
-// position: blockIdx.x = 2 n + half, half 0 the Key (min, scale) per channel
-// and the Key codes, half 1 the Value (min, scale) per member and the Value
-// codes. The members' rows are loaded into LDS once, all in one round trip;
-// the arithmetic is that of a single quantize step.
+// Moves `pieces` 16-byte pieces of each of `cnt` rows into LDS (row i at
+// rows + i * pieces * 16 bytes): piece tid % pieces of rows tid / pieces +
+// (512 / pieces) r, the row indices first, then every load at once. Rows past
+// `cnt` read row 0 of the prompt (present whenever a page is) and drop it.
+template <typename RowOf>
+__device__ __forceinline__ void pack_stage(uint4* rows, int pieces, int cnt, RowOf row_of,
+                                           const __half* __restrict__ src, int piece0) {
+  constexpr int kRounds = 4;  // cnt * pieces <= 4 * 512
+  const int tid = threadIdx.x, pc = tid % pieces, t0 = tid / pieces, step = kPackThreads / pieces;
+  int pos[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = t0 + r * step;
+    pos[r] = t < cnt ? row_of(t) : 0;
+  }
+  uint4 x[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    x[r] = reinterpret_cast<const uint4*>(src + size_t(pos[r]) * D)[piece0 + pc];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int t = t0 + r * step;
+    if (t < cnt) rows[t * pieces + pc] = x[r];
+  }
+}
+
+// One slice of page n's bytes, from its members' rows read from the prompt by
+// position, with the arithmetic of a single quantize step. A page is cut into
+// 2 S slices of at most 32 KiB of rows (S = G / 128 at G = 256, else 1):
+// blockIdx.x = 2 S n + q; q < S: the Key (min, scale) and codes of channels
+// [q D / S, (q + 1) D / S) over all members; q >= S: the Value (min, scale)
+// and codes of members [(q - S) G / S, (q - S + 1) G / S).
+template <int S>
 __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
     PrefillLens lens) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int n = blockIdx.x >> 1, half = blockIdx.x & 1, h = blockIdx.y, b = blockIdx.z;
+  const int n = blockIdx.x / (2 * S), q = blockIdx.x % (2 * S), h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.Hkv + h;
   if (n >= prefill_pages(a, lens.len[b])) return;
   const int G = a.G, P = a.P, tid = threadIdx.x;
   const int pc = min(P, G * n);
   const int n_valid = pc + G - min(P, pc + G);
-  __half* rows = reinterpret_cast<__half*>(lds_raw);  // member t's row at t * D
-  CodeThr* thr = reinterpret_cast<CodeThr*>(lds_raw + size_t(G) * D * sizeof(__half));
+  __half* rows = reinterpret_cast<__half*>(lds_raw);
+  CodeThr* thr = reinterpret_cast<CodeThr*>(lds_raw + kPackRowBytes);
   float* plo = reinterpret_cast<float*>(thr + 256);
   float* phi = plo + kPackThreads;
-  const __half* src = (half ? v : k) + size_t(bh) * max_len * D;
   const int32_t* pp = reinterpret_cast<const int32_t*>(a.base + a.off_page_pos) +
                       (size_t(bh) * a.nb_max + n) * G;
   uint8_t* pg = page_ptr(a, bh, n);
-  {
-    // thread tid moves 16-byte piece tid % 16 of members tid / 16 + 32 r: the
-    // positions first, then every row load at once (past the members, row 0
-    // of the prompt, which a page's existence guarantees, is read and dropped)
-    constexpr int kRounds = 256 * (D / 8) / kPackThreads;
-    const int c8 = tid % (D / 8), t0 = tid / (D / 8);
-    int pos[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int t = t0 + r * (kPackThreads / (D / 8));
-      pos[r] = t < n_valid ? pp[t] : 0;
-    }
-    uint4 x[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r)
-      x[r] = reinterpret_cast<const uint4*>(src + size_t(pos[r]) * D)[c8];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int t = t0 + r * (kPackThreads / (D / 8));
-      if (t < n_valid) reinterpret_cast<uint4*>(rows)[t * (D / 8) + c8] = x[r];
-    }
-  }
-  __syncthreads();
-  if (half == 0) {
-    // Key (min, scale) per channel: 4 partial scans, then one thread per channel
-    constexpr int kParts = kPackThreads / D;
+  auto member_pos = [&](int t) { return pp[t]; };
+  if (q < S) {
+    // Key slice: channels c0 .. c0 + DC - 1 of every member (row t at t * DC)
+    constexpr int DC = D / S, kParts = kPackThreads / DC;
+    const int c0 = q * DC;
+    pack_stage(reinterpret_cast<uint4*>(rows), DC / 8, n_valid, member_pos,
+               k + size_t(bh) * max_len * D, c0 / 8);
+    __syncthreads();
     {
-      const int c = tid % D, part = tid / D;
+      const int c = tid % DC, part = tid / DC;
       float lo = INFINITY, hi = -INFINITY;
 #pragma unroll 4
       for (int t = part; t < n_valid; t += kParts) {
-        const float x = __half2float(rows[t * D + c]);
+        const float x = __half2float(rows[t * DC + c]);
         lo = fminf(lo, x);
         hi = fmaxf(hi, x);
       }
@@ -1040,30 +1050,35 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
       phi[tid] = hi;
     }
     __syncthreads();
-    if (tid < D) {
+    if (tid < DC) {
       float lo = plo[tid], hi = phi[tid];
 #pragma unroll
       for (int p2 = 1; p2 < kParts; ++p2) {
-        lo = fminf(lo, plo[p2 * D + tid]);
-        hi = fmaxf(hi, phi[p2 * D + tid]);
+        lo = fminf(lo, plo[p2 * DC + tid]);
+        hi = fmaxf(hi, phi[p2 * DC + tid]);
       }
       if (n_valid == 0) lo = hi = 0.f;
+      const int c = c0 + tid;
       const uint32_t lo_b = meta_bits(lo);
       const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(hi, lo), 3.0f));
-      thr[(tid % 16) * (D / 16) + tid / 16] =
+      thr[(c % 16) * (D / 16) + c / 16] =
           code_thresholds(__half2float(__ushort_as_half(uint16_t(lo_b))),
                           __half2float(__ushort_as_half(uint16_t(sc_b))));
-      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[tid] = lo_b | (sc_b << 16);
+      reinterpret_cast<uint32_t*>(pg + kmeta_off(G))[c] = lo_b | (sc_b << 16);
     }
     __syncthreads();
     // codes, token-major: dword (t, j) = channels 16 j .. 16 j + 15 of member
-    // t (zero past the members); channel 16 j + cc's thresholds at cc * 8 + j
+    // t (zero past the members); channel 16 j + cc's thresholds at cc * 8 + j.
+    // The slice's dwords (t, j0 .. j0 + JS - 1) are gathered in LDS (over the
+    // partial minima, no longer read) and stored 16 bytes at a time.
     uint32_t* kc = reinterpret_cast<uint32_t*>(pg + kcode_off(G));
-    for (int w = tid; w < G * (D / 16); w += kPackThreads) {
-      const int t = w / (D / 16), j = w % (D / 16);
+    uint32_t* words = reinterpret_cast<uint32_t*>(plo);  // [G][JS]
+    constexpr int JS = DC / 16;
+    for (int w = tid; w < G * JS; w += kPackThreads) {
+      const int t = w / JS, jj = w % JS, j = c0 / 16 + jj;
       uint32_t word = 0;
       if (t < n_valid) {
-        const uint4* row = reinterpret_cast<const uint4*>(rows + t * D + 16 * j);
+        const uint4* row = reinterpret_cast<const uint4*>(rows + t * DC + 16 * jj);
         const uint4 r0 = row[0], r1 = row[1];
         const uint32_t hw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
@@ -1072,18 +1087,30 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
           word |= qcode(__half2float(__ushort_as_half(bits)), thr[cc * (D / 16) + j]) << (2 * cc);
         }
       }
-      kc[w] = word;
+      words[w] = word;
+    }
+    __syncthreads();
+    for (int w = tid; w < G * JS / 4; w += kPackThreads) {
+      const int t = w / (JS / 4), u = w % (JS / 4);
+      reinterpret_cast<uint4*>(kc + t * (D / 16) + c0 / 16)[u] =
+          reinterpret_cast<const uint4*>(words)[w];
     }
     return;
   }
-  // Value (min, scale) per member: 8 lanes per member, 16 channels each
-  // (rotated per member against bank conflicts), combined by lane swaps
+  // Value slice: members m0 .. m0 + MC - 1 (row t - m0 at (t - m0) * D)
+  const int MC = G / S, m0 = (q - S) * MC;
+  const int cnt = max(0, min(MC, n_valid - m0));
+  pack_stage(reinterpret_cast<uint4*>(rows), D / 8, cnt, [&](int t) { return pp[m0 + t]; },
+             v + size_t(bh) * max_len * D, 0);
+  __syncthreads();
+  // (min, scale) per member: 8 lanes per member, 16 channels each (rotated per
+  // member against bank conflicts), combined by lane swaps
   uint32_t* vmeta = reinterpret_cast<uint32_t*>(pg + vmeta_off(G));
-  for (int tb = 0; tb < G; tb += kPackThreads / 8) {
-    const int t = tb + (tid >> 3), part = tid & 7;
+  for (int tb = 0; tb < MC; tb += kPackThreads / 8) {
+    const int tl = tb + (tid >> 3), part = tid & 7, t = m0 + tl;
     float mn = INFINITY, mx = -INFINITY;
-    if (t < n_valid) {
-      const __half* row = rows + t * D;
+    if (tl < cnt) {
+      const __half* row = rows + tl * D;
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) {
         const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
@@ -1096,12 +1123,12 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
-    if (t < G && part == 0) {
-      if (t < n_valid) {
+    if (tl < MC && part == 0) {
+      if (tl < cnt) {
         const uint32_t mn_b = meta_bits(mn);
         const uint32_t sc_b = meta_bits(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
-        thr[t] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
-                                 __half2float(__ushort_as_half(uint16_t(sc_b))));
+        thr[tl] = code_thresholds(__half2float(__ushort_as_half(uint16_t(mn_b))),
+                                  __half2float(__ushort_as_half(uint16_t(sc_b))));
         vmeta[t] = mn_b | (sc_b << 16);
       } else {
         vmeta[t] = 0u;
@@ -1110,18 +1137,25 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
   }
   __syncthreads();
   // codes, channel-major: dword (c, j) = members 16 j .. 16 j + 15 of channel c
-  // (zero past the members)
+  // (zero past the members), gathered in LDS as [c][js] and stored 16 bytes at
+  // a time
   uint32_t* vc = reinterpret_cast<uint32_t*>(pg + vcode_off(G));
-  const int vdw = G / 16;
-  for (int w = tid; w < D * vdw; w += kPackThreads) {
-    const int c = w % D, j = w / D;
+  uint32_t* words = reinterpret_cast<uint32_t*>(plo);
+  const int vdw = G / 16, js = MC / 16;
+  for (int w = tid; w < D * js; w += kPackThreads) {
+    const int c = w % D, jj = w / D;
     uint32_t word = 0;
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) {
-      const int t = 16 * j + cc;
-      if (t < n_valid) word |= qcode(__half2float(rows[t * D + c]), thr[t]) << (2 * cc);
+      const int tl = 16 * jj + cc;
+      if (tl < cnt) word |= qcode(__half2float(rows[tl * D + c]), thr[tl]) << (2 * cc);
     }
-    vc[c * vdw + j] = word;
+    words[c * js + jj] = word;
+  }
+  __syncthreads();
+  for (int w = tid; w < D * js / 4; w += kPackThreads) {
+    const int c = w / (js / 4), u = w % (js / 4);
+    reinterpret_cast<uint4*>(vc + c * vdw + m0 / 16)[u] = reinterpret_cast<const uint4*>(words)[w];
   }
 }
 
@@ -1141,7 +1175,7 @@ size_t prefill_select_lds_bytes(int G, int P) {
   return ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15)) + size_t(P) * 2 * (sizeof(double) + 4);
 }
 
-// Groups per prefill segment: enough segments for about two walk work-groups
+// Groups per prefill segment: segments enough for up to two walk work-groups
 // per CU (at most 64, since a segment merges every earlier segment's pairs),
 // no more tokens than prefill_top_kernel holds, and page slots enough for the
 // segment's pairs (12 P bytes). One segment when the heads alone fill the GPU.
@@ -1152,15 +1186,19 @@ int prefill_segment(const Arena& a, int max_pages, int cus) {
   const int smax = kTopPerThread * kQuantThreads / a.G;
   if (smin > smax) return max_pages;
   const int64_t heads = int64_t(a.B) * a.Hkv;
-  const int64_t want =
-      std::min<int64_t>(64, std::max<int64_t>(1, (2 * int64_t(cus) + heads - 1) / heads));
+  const int64_t want = std::min<int64_t>(64, std::max<int64_t>(1, 2 * int64_t(cus) / heads));
   if (want == 1) return max_pages;
   const int seg = int((max_pages + want - 1) / want);
   return std::min(std::max(seg, smin), smax);
 }
 
 hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t max_len,
-                          const PrefillLens& lens, int max_pages, int cus, hipStream_t s) {
+                          const PrefillLens& lens, int max_pages, hipStream_t s) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
   const size_t lds_sel = prefill_select_lds_bytes(a.G, a.P);
   if (lds_sel > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_select_kernel),
@@ -1168,13 +1206,8 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
                                              int(lds_sel));
     if (e != hipSuccess) return e;
   }
-  const size_t lds_pack = pack_lds_bytes(a.G);
-  if (lds_pack > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_pack_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             int(lds_pack));
-    if (e != hipSuccess) return e;
-  }
+  const size_t lds_pack = pack_lds_bytes();
+  const int slices = a.G > 128 ? a.G / 128 : 1;
   const __half* kh = static_cast<const __half*>(k);
   const __half* vh = static_cast<const __half*>(v);
   if (max_pages > 0) {
@@ -1195,8 +1228,12 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
                      s, a, kh, vh, max_len, lens, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_pages == 0) return e;
-  hipLaunchKernelGGL(prefill_pack_kernel, dim3(2 * max_pages, a.Hkv, a.B), dim3(kPackThreads),
-                     lds_pack, s, a, kh, vh, max_len, lens);
+  if (slices == 2)
+    hipLaunchKernelGGL(prefill_pack_kernel<2>, dim3(4 * max_pages, a.Hkv, a.B),
+                       dim3(kPackThreads), lds_pack, s, a, kh, vh, max_len, lens);
+  else
+    hipLaunchKernelGGL(prefill_pack_kernel<1>, dim3(2 * max_pages, a.Hkv, a.B),
+                       dim3(kPackThreads), lds_pack, s, a, kh, vh, max_len, lens);
   return hipGetLastError();
 }
 
