@@ -186,10 +186,13 @@ ott_status_t ott_quantize_group(ott_handle_t h, void* stream, int32_t* n_seq_qua
  *              sequence b is row i (position i).
  *   h_len    : host int32 [B], 0 <= h_len[b] <= max_len (else OTT_ERR_INVALID_ARG),
  *              h_len[b] <= max_seq_len (else OTT_ERR_CAPACITY).
- *   Every sequence must be empty (else OTT_ERR_STATE, nothing enqueued). Three
- *   launches: every group token's squared Key norm at once, the pool walk (one
- *   work-group per (sequence, KV head), groups in position order), then every page
- *   at once; a no-op when every length is 0.
+ *   Every sequence must be empty (else OTT_ERR_STATE, nothing enqueued). Up to
+ *   four launches: every group token's squared Key norm at once; when the heads
+ *   alone do not fill the GPU, each segment of groups' P smallest (key, position)
+ *   pairs (the pool after a step holds the P smallest of all groups so far); the
+ *   pool walk, one work-group per (segment, sequence, KV head), groups in position
+ *   order from the merge of the earlier segments' pairs; then every page at once.
+ *   A no-op when every length is 0.
  */
 ott_status_t ott_prefill(ott_handle_t h, const void* d_k, const void* d_v, const int32_t* h_len,
                          int32_t max_len, void* stream);
