@@ -629,14 +629,43 @@ __device__ __forceinline__ double* prefill_norms(const Arena& a, int bh, int n) 
   return reinterpret_cast<double*>(page_ptr(a, bh, n));
 }
 
+// One work-group of G threads per page; wave w takes tokens 64 w .. 64 w + 63.
+// The rows reach each lane through LDS: a wave loads 8 half-rows (128 bytes
+// each) per instruction, stores them with rows padded to 9 pieces (against bank
+// conflicts), and each lane then sums its own token's channels in order.
 __global__ __launch_bounds__(256) void prefill_norms_kernel(Arena a, const __half* __restrict__ k,
                                                             int64_t max_len, PrefillLens lens) {
+  extern __shared__ uint4 tile_raw[];  // per wave: 64 half-rows of 8 pieces, padded to 9
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.Hkv + h;
   if (n >= prefill_pages(a, lens.len[b])) return;
-  const __half* kb = k + (size_t(bh) * max_len + size_t(n) * a.G) * D;
-  double* out = prefill_norms(a, bh, n);
-  for (int j = threadIdx.x; j < a.G; j += blockDim.x) out[j] = sq_norm_fp64(kb + size_t(j) * D);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint4* kb =
+      reinterpret_cast<const uint4*>(k + (size_t(bh) * max_len + size_t(n) * a.G + 64 * wv) * D);
+  uint4* t = tile_raw + wv * 64 * 9;
+  double acc = 0.0;
+  for (int hf = 0; hf < 2; ++hf) {
+    uint4 x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = kb[(8 * r + lane / 8) * (D / 8) + 8 * hf + lane % 8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t[(8 * r + lane / 8) * 9 + lane % 8] = x[r];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint4 w = t[lane * 9 + p];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double lo = double(__half2float(__ushort_as_half(uint16_t(ws[e] & 0xffffu))));
+        const double hi = double(__half2float(__ushort_as_half(uint16_t(ws[e] >> 16))));
+        acc = acc + lo * lo;
+        acc = acc + hi * hi;
+      }
+    }
+    __syncthreads();
+  }
+  prefill_norms(a, bh, n)[64 * wv + lane] = acc;
 }
 
 // Unsigned bits of a retention key that order as the key does: negative keys
@@ -836,9 +865,11 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, Pre
   }
 }
 
-// Two work-groups per CU (8 waves per SIMD): the walk's steps are short phases
-// between barriers, which a second work-group fills.
-__global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(8)))
+// 512 threads, four work-groups per CU (8 waves per SIMD): the walk's steps
+// are short phases between barriers, which the other work-groups fill.
+constexpr int kWalkThreads = 512;
+static_assert(kWalkThreads >= 256, "select_step gives each group token (G <= 256) a thread");
+__global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void prefill_select_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
     PrefillLens lens, int seg) {
@@ -1008,15 +1039,21 @@ __device__ __forceinline__ void pack_stage(uint4* rows, int pieces, int cnt, Row
 // One slice of page n's bytes, from its members' rows read from the prompt by
 // position, with the arithmetic of a single quantize step. A page is cut into
 // 2 S slices of at most 32 KiB of rows (S = G / 128 at G = 256, else 1):
-// blockIdx.x = 2 S n + q; q < S: the Key (min, scale) and codes of channels
-// [q D / S, (q + 1) D / S) over all members; q >= S: the Value (min, scale)
-// and codes of members [(q - S) G / S, (q - S + 1) G / S).
+// q < S: the Key (min, scale) and codes of channels [q D / S, (q + 1) D / S)
+// over all members; q >= S: the Value (min, scale) and codes of members
+// [(q - S) G / S, (q - S + 1) G / S). blockIdx.x = 2 n + q at S = 1. At S = 2
+// the slices of a page write the two halves of the same 128-byte lines (Key
+// codes of a member, Value codes of a channel), so they run on one XCD (work-
+// group i runs on XCD i mod 8, and the x dimension is padded to a multiple of
+// 32), where the halves meet in its L2: blockIdx.x = 32 (n / 8) + 8 q + n % 8.
 template <int S>
 __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
     PrefillLens lens) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  const int n = blockIdx.x / (2 * S), q = blockIdx.x % (2 * S), h = blockIdx.y, b = blockIdx.z;
+  const int xb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = S == 1 ? xb / 2 : (xb / 32) * 8 + xb % 8;
+  const int q = S == 1 ? xb % 2 : (xb / 8) % 4;
   const int bh = b * a.Hkv + h;
   if (n >= prefill_pages(a, lens.len[b])) return;
   const int G = a.G, P = a.P, tid = threadIdx.x;
@@ -1175,7 +1212,7 @@ size_t prefill_select_lds_bytes(int G, int P) {
   return ((quant_lds_bytes(G, P, 0) + 15) & ~size_t(15)) + size_t(P) * 2 * (sizeof(double) + 4);
 }
 
-// Groups per prefill segment: segments enough for up to two walk work-groups
+// Groups per prefill segment: segments enough for up to four walk work-groups
 // per CU (at most 64, since a segment merges every earlier segment's pairs),
 // no more tokens than prefill_top_kernel holds, and page slots enough for the
 // segment's pairs (12 P bytes). One segment when the heads alone fill the GPU.
@@ -1186,7 +1223,7 @@ int prefill_segment(const Arena& a, int max_pages, int cus) {
   const int smax = kTopPerThread * kQuantThreads / a.G;
   if (smin > smax) return max_pages;
   const int64_t heads = int64_t(a.B) * a.Hkv;
-  const int64_t want = std::min<int64_t>(64, std::max<int64_t>(1, 2 * int64_t(cus) / heads));
+  const int64_t want = std::min<int64_t>(64, std::max<int64_t>(1, 4 * int64_t(cus) / heads));
   if (want == 1) return max_pages;
   const int seg = int((max_pages + want - 1) / want);
   return std::min(std::max(seg, smin), smax);
@@ -1211,8 +1248,8 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
   const __half* kh = static_cast<const __half*>(k);
   const __half* vh = static_cast<const __half*>(v);
   if (max_pages > 0) {
-    hipLaunchKernelGGL(prefill_norms_kernel, dim3(max_pages, a.Hkv, a.B), dim3(256), 0, s, a, kh,
-                       max_len, lens);
+    hipLaunchKernelGGL(prefill_norms_kernel, dim3(max_pages, a.Hkv, a.B), dim3(a.G),
+                       size_t(a.G) * 9 * sizeof(uint4), s, a, kh, max_len, lens);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1224,12 +1261,12 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(prefill_select_kernel, dim3(nseg, a.Hkv, a.B), dim3(kQuantThreads), lds_sel,
+  hipLaunchKernelGGL(prefill_select_kernel, dim3(nseg, a.Hkv, a.B), dim3(kWalkThreads), lds_sel,
                      s, a, kh, vh, max_len, lens, seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_pages == 0) return e;
   if (slices == 2)
-    hipLaunchKernelGGL(prefill_pack_kernel<2>, dim3(4 * max_pages, a.Hkv, a.B),
+    hipLaunchKernelGGL(prefill_pack_kernel<2>, dim3(32 * ((max_pages + 7) / 8), a.Hkv, a.B),
                        dim3(kPackThreads), lds_pack, s, a, kh, vh, max_len, lens);
   else
     hipLaunchKernelGGL(prefill_pack_kernel<1>, dim3(2 * max_pages, a.Hkv, a.B),
