@@ -869,6 +869,7 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, Pre
 // are short phases between barriers, which the other work-groups fill.
 constexpr int kWalkThreads = 512;
 static_assert(kWalkThreads >= 256, "select_step gives each group token (G <= 256) a thread");
+static_assert(kWalkThreads >= kMaxPool, "the start-pool merge gives each pair a thread");
 __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void prefill_select_kernel(
     Arena a, const __half* __restrict__ k, const __half* __restrict__ v, int64_t max_len,
@@ -909,13 +910,24 @@ void prefill_select_kernel(
   // merges alternate buffers and end in buffer g0 & 1, which step g0 reads
   {
     int x = (g0 + sg) & 1, pc = 0;
-    const int cb = min(P, seg * G);
+    const int cb = min(P, seg * G);  // <= 512 = blockDim: one pair per thread
+    // the next segment's pairs travel in registers while this merge runs
+    double nk = 0.0;
+    int np = 0;
+    if (sg > 0 && tid < cb) {
+      nk = *seg_top_key(a, bh, 0, tid);
+      np = *seg_top_pos(a, bh, 0, tid);
+    }
     for (int i = 0; i < sg; ++i) {
-      for (int t = tid; t < cb; t += blockDim.x) {
-        s.n2[t] = *seg_top_key(a, bh, i * seg, t);
-        s.pos[t] = *seg_top_pos(a, bh, i * seg, t);
+      if (tid < cb) {
+        s.n2[tid] = nk;
+        s.pos[tid] = np;
       }
       __syncthreads();
+      if (i + 1 < sg && tid < cb) {
+        nk = *seg_top_key(a, bh, (i + 1) * seg, tid);
+        np = *seg_top_pos(a, bh, (i + 1) * seg, tid);
+      }
       const int npc = min(P, pc + cb);
       for (int t = tid; t < pc + cb; t += blockDim.x) {
         const bool in_pool = t < pc;
