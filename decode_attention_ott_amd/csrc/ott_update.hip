@@ -250,31 +250,64 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
   //    ascending (key, position) order and every pool position precedes every
   //    group position, so a pool entry's rank is its index plus the group keys
   //    below its key, and a group token's rank is the pool keys at or below its
-  //    key (a binary search) plus the group tokens below it. The comparisons
-  //    against the group are split over `parts` threads per candidate
-  //    (branch-free, so the LDS reads pipeline) and summed with LDS atomics.
-  const int parts = max(1, int(blockDim.x) / NC);
-  const int span = (G + parts - 1) / parts;
+  //    key (a binary search) plus the group tokens below it. Once the pool is
+  //    full, a group token whose key is not below the pool's largest key ranks
+  //    after all P pool entries: it is a member whatever its exact rank (set to
+  //    NC), and neither it nor its comparisons change any other rank. So only
+  //    the group tokens below that key (list `cl`, usually a few once the
+  //    prompt is long) are counted, each against the others of the list. The
+  //    comparisons are split over `parts` threads per candidate (branch-free,
+  //    so the LDS reads pipeline) and summed with LDS atomics.
   for (int i = tid; i < NC; i += blockDim.x) {
     s.rank[i] = 0;
     s.idx[i] = 0;
   }
   __syncthreads();
-  for (int x = tid; x < NC * parts; x += blockDim.x) {
-    const int i = x % NC, part = x / NC;
-    const int j0 = pc + part * span, j1 = min(NC, j0 + span);
+  const bool full = pc == P;
+  int nC = G;  // group tokens that can enter the pool
+  if (full) {
+    const double kmax = P > 0 ? s.n2[pc - 1] : -INFINITY;
+    const bool in_c = tid < G && s.n2[pc + tid] < kmax;
+    if (tid < G && !in_c) s.rank[pc + tid] = NC;
+    const uint64_t ball = __ballot(in_c);
+    const int lane = tid & 63, wv = tid >> 6;
+    if (lane == 0 && tid < G) s.wsum[wv] = __popcll(ball);
+    __syncthreads();
+    int before = 0;
+    nC = 0;
+    for (int w = 0; w < (G + 63) / 64; ++w) {
+      nC += s.wsum[w];
+      if (w < wv) before += s.wsum[w];
+    }
+    if (in_c)
+      s.mem[before + __builtin_amdgcn_mbcnt_hi(uint32_t(ball >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(uint32_t(ball), 0))] =
+          pc + tid;
+    __syncthreads();
+  }
+  // candidate k of the list: pool entries first, then the group tokens that
+  // can enter (in group order)
+  const int M = pc + nC;
+  auto cand = [&](int k) { return k < pc ? k : (full ? s.mem[k - pc] : k); };
+  const int parts = M > 0 ? max(1, int(blockDim.x) / M) : 1;
+  const int span = (nC + parts - 1) / parts;
+  for (int x = tid; x < M * parts; x += blockDim.x) {
+    const int e = x % M, part = x / M;
+    const int i = cand(e);
+    const int k0 = pc + part * span, k1 = min(M, k0 + span);
     const double ni = s.n2[i];
     const int pi = s.pos[i];
     int r = 0;
     if (i < pc) {
 #pragma unroll 4
-      for (int j = j0; j < j1; ++j) r += int(s.n2[j] < ni);
+      for (int k = k0; k < k1; ++k) r += int(s.n2[cand(k)] < ni);
       if (part == 0) r += i;
     } else {
 #pragma unroll 4
-      for (int j = j0; j < j1; ++j) {
-        const double nj = s.n2[j];
-        const int pj = s.pos[j];
+      for (int k = k0; k < k1; ++k) {
+        const int jj = cand(k);
+        const double nj = s.n2[jj];
+        const int pj = s.pos[jj];
         r += int(nj < ni) | (int(nj == ni) & int(pj < pi));
       }
       if (part == 0) {  // pool keys <= ni
