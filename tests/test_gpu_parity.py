@@ -166,6 +166,24 @@ def test_signed_zeros_and_norm_order():
     run_case(w, plant=_plant_zeros_and_norm_ties, state_every_step=True)
 
 
+def _keys_on_a_grid(K, V):
+    """Keys rounded to the integers -2..2: most squared norms are small
+    integers shared by many tokens."""
+    K[...] = np.clip(np.rint(K.astype(np.float32)), -2.0, 2.0).astype(np.float16)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_tied_keys_rank_by_position(rule):
+    """Most keys tie, and many group keys equal the pool's largest key (such a
+    token stays out of a full pool: the pool entry's position is lower). The
+    prefill's segment selection and walk and the stepwise quantize steps rank
+    ties by position as the oracle does; the largest-norm rule negates the
+    keys (a zero norm gives -0)."""
+    w = small(f"ties{rule}", B=3, Hkv=2, G=64, R=16, P=40, L=(1500, 2600), steps=70,
+              seed=95 + rule, retention=rule)
+    run_case(w, plant=_keys_on_a_grid, state_every_step=True)
+
+
 def test_large_scores_are_safe():
     """Queries scaled x16: scores in the hundreds; the online softmax must
     rescale without overflow (softmax shift invariance)."""
