@@ -1185,19 +1185,22 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
   pack_stage(reinterpret_cast<uint4*>(rows), D / 8, cnt, [&](int t) { return pp[m0 + t]; },
              v + size_t(bh) * max_len * D, 0);
   __syncthreads();
-  // (min, scale) per member: 8 lanes per member, 16 channels each (rotated per
-  // member against bank conflicts), combined by lane swaps
+  // (min, scale) per member: 8 lanes per member, 8 channel pairs each (4-byte
+  // reads, rotated per member against bank conflicts), combined by lane swaps
   uint32_t* vmeta = reinterpret_cast<uint32_t*>(pg + vmeta_off(G));
+  const uint32_t* rows2 = reinterpret_cast<const uint32_t*>(rows);  // channel pairs
   for (int tb = 0; tb < MC; tb += kPackThreads / 8) {
     const int tl = tb + (tid >> 3), part = tid & 7, t = m0 + tl;
     float mn = INFINITY, mx = -INFINITY;
     if (tl < cnt) {
-      const __half* row = rows + tl * D;
+      const uint32_t* row = rows2 + tl * (D / 2);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const float x = __half2float(row[(part * (D / 8) + i + 2 * t) % D]);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
+      for (int i = 0; i < D / 16; ++i) {
+        const uint32_t w = row[(part * (D / 16) + i + tl) % (D / 2)];
+        const float x0 = __half2float(__ushort_as_half(uint16_t(w & 0xffffu)));
+        const float x1 = __half2float(__ushort_as_half(uint16_t(w >> 16)));
+        mn = fminf(mn, fminf(x0, x1));
+        mx = fmaxf(mx, fmaxf(x0, x1));
       }
     }
 #pragma unroll
@@ -1219,20 +1222,27 @@ __global__ __launch_bounds__(kPackThreads) void prefill_pack_kernel(
   }
   __syncthreads();
   // codes, channel-major: dword (c, j) = members 16 j .. 16 j + 15 of channel c
-  // (zero past the members), gathered in LDS as [c][js] and stored 16 bytes at
-  // a time
+  // (zero past the members), a lane taking channels c and c + 1 (one 4-byte
+  // read per member, one threshold read for both), gathered in LDS as [c][js]
+  // and stored 16 bytes at a time
   uint32_t* vc = reinterpret_cast<uint32_t*>(pg + vcode_off(G));
   uint32_t* words = reinterpret_cast<uint32_t*>(plo);
   const int vdw = G / 16, js = MC / 16;
-  for (int w = tid; w < D * js; w += kPackThreads) {
-    const int c = w % D, jj = w / D;
-    uint32_t word = 0;
+  for (int w = tid; w < (D / 2) * js; w += kPackThreads) {
+    const int c2 = w % (D / 2), jj = w / (D / 2);
+    uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) {
       const int tl = 16 * jj + cc;
-      if (tl < cnt) word |= qcode(__half2float(rows[tl * D + c]), thr[tl]) << (2 * cc);
+      if (tl < cnt) {
+        const uint32_t x = rows2[tl * (D / 2) + c2];
+        const CodeThr q = thr[tl];
+        w0 |= qcode(__half2float(__ushort_as_half(uint16_t(x & 0xffffu))), q) << (2 * cc);
+        w1 |= qcode(__half2float(__ushort_as_half(uint16_t(x >> 16))), q) << (2 * cc);
+      }
     }
-    words[c * js + jj] = word;
+    words[(2 * c2) * js + jj] = w0;
+    words[(2 * c2 + 1) * js + jj] = w1;
   }
   __syncthreads();
   for (int w = tid; w < D * js / 4; w += kPackThreads) {
