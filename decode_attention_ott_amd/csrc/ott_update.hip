@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "ott_device.h"
 
@@ -1269,6 +1270,9 @@ size_t prefill_select_lds_bytes(int G, int P) {
 
 // Groups per prefill segment: segments enough for up to four walk work-groups
 // per CU (at most 64, since a segment merges every earlier segment's pairs),
+// and at least sqrt(pages) / 2 groups (a walk step costs a few merges, so
+// steps and merges balance there: at 32 heads of 4K tokens one-group segments
+// took 145 us and three-group ones 98),
 // no more tokens than prefill_top_kernel holds, and page slots enough for the
 // segment's pairs (12 P bytes). One segment when the heads alone fill the GPU.
 int prefill_segment(const Arena& a, int max_pages, int cus) {
@@ -1280,7 +1284,8 @@ int prefill_segment(const Arena& a, int max_pages, int cus) {
   const int64_t heads = int64_t(a.B) * a.Hkv;
   const int64_t want = std::min<int64_t>(64, std::max<int64_t>(1, 4 * int64_t(cus) / heads));
   if (want == 1) return max_pages;
-  const int seg = int((max_pages + want - 1) / want);
+  const int balance = int(std::ceil(std::sqrt(double(max_pages)) / 2));
+  const int seg = std::max(int((max_pages + want - 1) / want), balance);
   return std::min(std::max(seg, smin), smax);
 }
 
