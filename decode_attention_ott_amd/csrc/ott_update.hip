@@ -230,8 +230,11 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
   const int NC = pc + G;          // candidates: pool + group
   const int npc = min(P, NC);     // pool tokens after this step
 
-  // 1. candidates; squared Key norms of the group, fp64 in channel order
+  // 1. candidates; squared Key norms of the group, fp64 in channel order;
+  //    their rank and member-index counters start at 0
   for (int i = tid; i < NC; i += blockDim.x) {
+    s.rank[i] = 0;
+    s.idx[i] = 0;
     if (i < pc) {
       s.n2[i] = pkey[i];
       s.pos[i] = ppos[i];
@@ -259,11 +262,6 @@ __device__ __forceinline__ void select_step(const Arena& a, int nb, const double
   //    prompt is long) are counted, each against the others of the list. The
   //    comparisons are split over `parts` threads per candidate (branch-free,
   //    so the LDS reads pipeline) and summed with LDS atomics.
-  for (int i = tid; i < NC; i += blockDim.x) {
-    s.rank[i] = 0;
-    s.idx[i] = 0;
-  }
-  __syncthreads();
   const bool full = pc == P;
   int nC = G;  // group tokens that can enter the pool
   if (full) {
