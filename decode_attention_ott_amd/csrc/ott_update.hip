@@ -647,8 +647,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(Arena a, Quanti
 //       the page's member list; the last segment then writes the final pool
 //       and the one before it (the two pool buffers single steps would leave),
 //       the window and the counters.
-//   prefill_pack_kernel    one work-group per page: the page bytes from its
-//       members' rows, read from the prompt by position.
+//   prefill_pack_kernel    one work-group per page slice (the Key channels or
+//       the Value members of a page, at most 32 KiB of rows): its bytes from
+//       the members' rows, read from the prompt by position.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int prefill_pages(const Arena& a, int L) {
   return L >= a.R + a.G ? (L - a.R) / a.G : 0;
