@@ -728,7 +728,10 @@ __device__ __forceinline__ int32_t* seg_top_pos(const Arena& a, int bh, int g0, 
   return reinterpret_cast<int32_t*>(seg_top_at(a, bh, g0, 8 * size_t(a.P) + 4 * size_t(i)));
 }
 
-constexpr int kTopPerThread = 16;  // a segment holds at most 16 * 1024 tokens
+// 512 threads with 16 keys each: two work-groups per CU (81 VGPRs); 1024
+// threads took 59 against 38 us for the 24 segments of 40 heads at 128K
+constexpr int kTopThreads = 512;
+constexpr int kTopPerThread = 16;  // a segment holds at most 16 * 512 tokens
 constexpr int kMaxPool = 512;
 
 // The min(P, seg G) smallest (key, position) pairs of segment blockIdx.x's
@@ -738,12 +741,12 @@ constexpr int kMaxPool = 512;
 // The pairs below the final boundary are all taken; on it, the first ones in
 // position order. Then ranked by (key, position). The last segment of a
 // sequence has no successor to read its pairs and is skipped.
-__global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, PrefillLens lens,
+__global__ __launch_bounds__(kTopThreads) void prefill_top_kernel(Arena a, PrefillLens lens,
                                                                     int seg) {
   __shared__ uint32_t hist[256];
-  __shared__ uint64_t red[2][kQuantThreads / 64];
+  __shared__ uint64_t red[2][kTopThreads / 64];
   __shared__ int pick[3];  // digit, pairs below it, pairs on it
-  __shared__ int wcnt[kQuantThreads / 64];
+  __shared__ int wcnt[kTopThreads / 64];
   __shared__ int n_sel;
   __shared__ double sel_k[kMaxPool];
   __shared__ int32_t sel_p[kMaxPool];
@@ -756,13 +759,13 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, Pre
   const int G = a.G, n = seg * G, take = min(a.P, n);
   if (take == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  constexpr int kWavesT = kQuantThreads / 64;
+  constexpr int kWavesT = kTopThreads / 64;
 
   uint64_t u[kTopPerThread];
   uint64_t mn = ~0ull, mx = 0;
 #pragma unroll
   for (int k = 0; k < kTopPerThread; ++k) {
-    const int j = tid + k * kQuantThreads;
+    const int j = tid + k * kTopThreads;
     u[k] = 0;
     if (j < n) {
       const double x = retention_key(prefill_norms(a, bh, g0 + j / G)[j % G], g0 * G + j,
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, Pre
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kTopPerThread; ++k)
-        if (tid + k * kQuantThreads < n && shr64(u[k], lo) == pre)
+        if (tid + k * kTopThreads < n && shr64(u[k], lo) == pre)
           atomicAdd(&hist[uint32_t(u[k] >> nlo) & mask], 1u);
       __syncthreads();
       if (wv == 0) {
@@ -843,13 +846,13 @@ __global__ __launch_bounds__(kQuantThreads) void prefill_top_kernel(Arena a, Pre
   int tie_base = 0;
 #pragma unroll
   for (int k = 0; k < kTopPerThread; ++k) {
-    const int j = tid + k * kQuantThreads;
+    const int j = tid + k * kTopThreads;
     const bool valid = j < n;
     const uint64_t hb = shr64(u[k], lo);
     const bool tie = valid && hb == pre;
     bool taken = valid && hb < pre;
     if (split) {
-      if (k * kQuantThreads >= n) break;  // uniform
+      if (k * kTopThreads >= n) break;  // uniform
       const uint64_t ball = __ballot(tie);
       const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(ball >> 32),
                                                   __builtin_amdgcn_mbcnt_lo(uint32_t(ball), 0));
@@ -1272,13 +1275,13 @@ size_t prefill_select_lds_bytes(int G, int P) {
 // and at least sqrt(pages) / 2 groups (a walk step costs a few merges, so
 // steps and merges balance there: at 32 heads of 4K tokens one-group segments
 // took 145 us and three-group ones 98),
-// no more tokens than prefill_top_kernel holds, and page slots enough for the
+// no more tokens than prefill_top_kernel holds (8K), and page slots enough for the
 // segment's pairs (12 P bytes). One segment when the heads alone fill the GPU.
 int prefill_segment(const Arena& a, int max_pages, int cus) {
   if (max_pages <= 1 || a.P == 0) return max(max_pages, 1);
   const size_t f = (size_t(a.page_bytes) - 8 * size_t(a.G)) & ~size_t(7);
   const int smin = int((12 * size_t(a.P) + f - 1) / f);
-  const int smax = kTopPerThread * kQuantThreads / a.G;
+  const int smax = kTopPerThread * kTopThreads / a.G;
   if (smin > smax) return max_pages;
   const int64_t heads = int64_t(a.B) * a.Hkv;
   const int64_t want = std::min<int64_t>(64, std::max<int64_t>(1, 4 * int64_t(cus) / heads));
@@ -1315,7 +1318,7 @@ hipError_t launch_prefill(const Arena& a, const void* k, const void* v, int64_t 
   const int seg = prefill_segment(a, max_pages, cus);
   const int nseg = max_pages > 0 ? (max_pages + seg - 1) / seg : 1;
   if (nseg > 1) {
-    hipLaunchKernelGGL(prefill_top_kernel, dim3(nseg - 1, a.Hkv, a.B), dim3(kQuantThreads), 0, s,
+    hipLaunchKernelGGL(prefill_top_kernel, dim3(nseg - 1, a.Hkv, a.B), dim3(kTopThreads), 0, s,
                        a, lens, seg);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
